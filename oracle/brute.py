@@ -1,0 +1,53 @@
+"""Pure-Python loop versions of the definitions, for tiny inputs.
+
+Test infrastructure only (see the package docstring). These are written as
+explicit scalar loops with ``math`` so that they share no vectorisation,
+broadcasting or library path with ``wan_ref``; they serve as one of the pins
+of the vectorised oracle on tiny grids.
+"""
+
+import math
+
+
+def attention_brute(q, k, v, scale):
+    """Row-by-row softmax attention with exact summation (math.fsum).
+    q, k, v: lists of lists of floats. Returns (o, lse) as lists."""
+    o, lse = [], []
+    for qi in q:
+        s = [scale * math.fsum(qi[c] * kj[c] for c in range(len(qi))) for kj in k]
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        den = math.fsum(p)
+        row = [math.fsum(p[j] * v[j][c] for j in range(len(k))) / den for c in range(len(v[0]))]
+        o.append(row)
+        lse.append(m + math.log(den))
+    return o, lse
+
+
+def rms_scale_brute(row, gamma, eps):
+    """x_c / sqrt(mean over all channels of x^2 + eps) * gamma_c, one token."""
+    ms = math.fsum(x * x for x in row) / len(row)
+    r = 1.0 / math.sqrt(ms + eps)
+    return [row[c] * r * gamma[c] for c in range(len(row))]
+
+
+def rope_angle_brute(pair, f, y, w, head_dim=128, split=(44, 42, 42), theta=10000.0):
+    """Rotation angle of channel pair ``pair`` of a head at grid position (f, y, w)."""
+    start = 0
+    for pos, n in zip((f, y, w), split):
+        if pair < start + n // 2:
+            j = pair - start
+            return pos * theta ** (-2.0 * j / n)
+        start += n // 2
+    raise IndexError(pair)
+
+
+def rope_head_brute(vec, f, y, w, theta=10000.0, split=(44, 42, 42)):
+    """Rotate the interleaved pairs of one head vector."""
+    out = list(vec)
+    for p in range(len(vec) // 2):
+        phi = rope_angle_brute(p, f, y, w, len(vec), split, theta)
+        a, b = vec[2 * p], vec[2 * p + 1]
+        out[2 * p] = a * math.cos(phi) - b * math.sin(phi)
+        out[2 * p + 1] = a * math.sin(phi) + b * math.cos(phi)
+    return out

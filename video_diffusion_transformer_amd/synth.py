@@ -1,0 +1,43 @@
+"""Seeded synthetic inputs for the self-attention step.
+
+This module holds no arithmetic of the method: it only draws the packed QKV
+activations (independent N(0, 1) values rounded to bfloat16) and the two RMSNorm
+weight vectors (1 + 0.1 * N(0, 1), rounded to bfloat16), from a torch generator
+seeded per workload. Both the HIP path and the CPU oracle receive exactly these
+tensors.
+
+The pages measure on the MLPerf Wan2.2 720p workload, whose activations are not
+available; these draws stand in for it with the same shapes. Dense attention
+timing does not depend on the values.
+"""
+
+import torch
+
+
+def make_qkv(B, S, heads, head_dim=128, seed=0, device="cpu", chunk_tokens=8192):
+    """Packed [B, S, 3 * heads * head_dim] bfloat16 tensor of N(0, 1) draws.
+
+    Drawn in chunks of ``chunk_tokens`` rows (float32, then rounded to bf16) so
+    that the float32 temporary stays small. The same (seed, device, chunking)
+    always gives the same tensor."""
+    D = heads * head_dim
+    out = torch.empty((B, S, 3 * D), dtype=torch.bfloat16, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    flat = out.view(B * S, 3 * D)
+    for i in range(0, B * S, chunk_tokens):
+        n = min(chunk_tokens, B * S - i)
+        flat[i:i + n] = torch.randn((n, 3 * D), generator=gen, device=device,
+                                    dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
+def make_gammas(D, seed=0, device="cpu"):
+    """RMSNorm weights for Q and K, each [D] bfloat16 = bf16(1 + 0.1 * N(0, 1)),
+    drawn on the CPU from their own generator so they do not depend on the
+    device."""
+    gen = torch.Generator()
+    gen.manual_seed(10_000 + seed)
+    g = 1.0 + 0.1 * torch.randn((2, D), generator=gen, dtype=torch.float32)
+    g = g.to(torch.bfloat16).to(device)
+    return g[0].contiguous(), g[1].contiguous()
