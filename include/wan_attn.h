@@ -1,0 +1,151 @@
+/*
+ * wan_attn.h -- C ABI of the Wan2.2 DiT self-attention hot path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One self-attention step of the Wan2.2 video diffusion transformer:
+ *
+ *   packed [Q|K|V] projection output (bf16, one allocation)
+ *     -> wan_qknorm_rope : RMSNorm of Q and of K over the full model width,
+ *                          x gamma, rounded to bf16, 3-D rotary embedding over
+ *                          the (frame, row, column) token grid, rounded to bf16,
+ *                          written back in place
+ *     -> wan_attn_fwd    : bidirectional (unmasked) softmax attention of every
+ *                          head over every token, read straight from the packed
+ *                          buffer
+ *   (fp8 variant: wan_qkv_quant_fp8, then wan_attn_fwd_fp8)
+ *
+ * Sources (web pages on Wan2.2, cited by title and section):
+ *   "Optimizing High-Quality Offline Video Generation" (AWS Neuron docs):
+ *       "Grounding in an output spec" (the token grid and S), "Overview"
+ *       (bidirectional DiT), "Tensor parallelism" (40 heads x 128), "Context
+ *       parallelism" (K/V chunks and the per-chunk log-sum-exp merge).
+ *   "[visual_gen] Optimize Wan2.2 Dataflow" (TensorRT-LLM pull request):
+ *       change 1 (Q, K read as strided views of the fused QKV allocation and
+ *       updated in place, [Q | K | V] preserved), "Fused Q/K Norm and RoPE"
+ *       (fp32 norm -> bf16 -> fp32 RoPE -> bf16), the review comments (the
+ *       norm spans num_heads * head_dim; weight index head * head_dim + dim),
+ *       change 2 (amax -> E4M3 inverse scale -> quantise), "Fallback
+ *       Behavior" (preconditions of the packed path).
+ *   "Wan2.2 Text-to-Video" (vLLM-Omni recipe): head_dim == 128, and an
+ *       unsupported configuration raises instead of degrading silently.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Layout. The packed buffer is row-major [B, S, 3*D] with D = heads *
+ *    head_dim: token (b, s) owns the row at element offset (b*S + s)*3*D;
+ *    Q of head h sits at +h*head_dim, K at +D + h*head_dim, V at +2*D +
+ *    h*head_dim. Token s of a T x H x W grid is frame f = s / (H*W), row
+ *    y = (s / W) % H, column x = s % W.
+ *  * Pointers are device pointers (hipMalloc / torch CUDA tensors) unless a
+ *    parameter says otherwise. The caller owns every pointer; the library never
+ *    frees or retains caller memory. Buffers must be 16-byte aligned (4-byte for
+ *    fp32 vectors).
+ *  * stream is a hipStream_t (NULL = the default stream). Every entry point
+ *    only enqueues work on it and returns; the caller synchronises. Device-side
+ *    faults surface at that synchronisation, not in the return code.
+ *  * Return value: WAN_OK (0) or a negative wan_status. Argument validation runs
+ *    first, touches no memory and makes no HIP call; on any error nothing is
+ *    written. There is no fallback path and no environment variable.
+ *  * Empty input (B == 0 or S == 0) is a valid no-op that returns WAN_OK
+ *    without looking at the pointers.
+ *  * head_dim must be 128 (the only head width of the model and of its
+ *    kernels); heads must be 1..256.
+ *  * Calls are thread-safe; calls on different streams may overlap unless a
+ *    function says otherwise.
+ */
+#ifndef WAN_ATTN_H
+#define WAN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WAN_ABI_VERSION 1
+
+typedef enum {
+  WAN_OK = 0,
+  WAN_E_NULL = -1,        /* a required pointer is NULL */
+  WAN_E_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
+  WAN_E_UNSUPPORTED = -3, /* head_dim != 128 or heads outside 1..256 */
+  WAN_E_ALIGN = -4,       /* a pointer is not aligned as required */
+  WAN_E_ALIAS = -5,       /* an output overlaps an input it must not overlap */
+  WAN_E_OVERFLOW = -6,    /* a size product overflows int64, or S exceeds 2^31-1 */
+  WAN_E_HIP = -7,         /* a HIP runtime call or kernel launch failed */
+  WAN_E_NOMEM = -8,       /* a library-owned table could not be allocated */
+  WAN_E_VALUE = -9        /* a scalar argument is out of range (eps, theta, scale) */
+} wan_status;
+
+/* Version of this ABI (WAN_ABI_VERSION of the built library). */
+int wan_abi_version(void);
+
+/* Static, human-readable text for a wan_status value. Never NULL. */
+const char *wan_status_str(int status);
+
+/*
+ * wan_qknorm_rope -- in-place Q/K RMSNorm + bf16 rounding point + 3-D RoPE.
+ *
+ * For every token row and separately for Q and K ("Optimize Wan2.2 Dataflow":
+ * change 1, "Fused Q/K Norm and RoPE", and the review comments):
+ *   ms   = mean over all D channels of x^2        (fp32 accumulation)
+ *   n_c  = bf16( x_c * (ms + eps)^-1/2 * gamma[c] ), c = h*head_dim + i
+ *   RoPE on interleaved pairs (2j, 2j+1) of each head: pairs 0..21 rotate with
+ *   the frame index, 22..42 with the row index, 43..63 with the column index
+ *   (the 44/42/42 channel split of Wan2.2's 3-D rotary embedding); pair j' of an
+ *   axis with d_a channels has angle pos * theta^(-2 j' / d_a);
+ *   out = bf16( rotate(n) ), fp32 arithmetic, stored over Q and K in place.
+ *
+ *   qkv      bf16 [B, S, 3*D], S = T*H*W, in/out. Q and K are overwritten; V is
+ *            never read or written.
+ *   gamma_q  bf16 [D], RMSNorm weight of Q (norm_q); read only.
+ *   gamma_k  bf16 [D], RMSNorm weight of K (norm_k); read only.
+ *   B        batch (2 = the classifier-free-guidance pair), >= 0.
+ *   T, H, W  token grid (frames, rows, columns), each >= 0.
+ *   heads    number of heads (40 for Wan2.2-A14B); head_dim must be 128.
+ *   eps      RMSNorm epsilon (1e-6), finite and >= 0.
+ *   theta    RoPE base (10000), finite and > 0.
+ *
+ * The cos/sin tables of a (device, T, H, W, theta) are built once on the host
+ * in double precision, rounded to fp32, and kept in a library-owned device
+ * allocation for the life of the process (its first call per shape therefore
+ * allocates and copies synchronously; later calls only launch).
+ * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN (qkv, gammas
+ * 16-byte), WAN_E_ALIAS (a gamma inside qkv), WAN_E_OVERFLOW, WAN_E_VALUE,
+ * WAN_E_NOMEM, WAN_E_HIP.
+ */
+int wan_qknorm_rope(void *qkv, const void *gamma_q, const void *gamma_k,
+                    int64_t B, int64_t T, int64_t H, int64_t W,
+                    int64_t heads, int64_t head_dim,
+                    float eps, float theta, void *stream);
+
+/*
+ * wan_attn_fwd -- bidirectional multi-head softmax attention on the packed
+ * buffer (AWS page "Overview": the DiT denoiser is bidirectional; "Tensor
+ * parallelism": 40 heads of 128).
+ *
+ *   out[b, s, h*128 + i] = sum_t p(s,t) V[b,t,h,i],
+ *   p(s,t) = softmax_t( Q[b,s,h,:] . K[b,t,h,:] * softmax_scale )
+ * over every key t < S; no mask, no dropout. QK^T and PV run on bf16 MFMA with
+ * fp32 accumulation; the softmax is fp32; P is rounded to bf16 for PV.
+ *
+ *   qkv            bf16 [B, S, 3*D] packed buffer (normally after
+ *                  wan_qknorm_rope); read only.
+ *   out            bf16 [B, S, D], head h at channels h*128..; written fully.
+ *                  Must not overlap qkv.
+ *   lse            fp32 [B, heads, S] natural-log log-sum-exp of every score
+ *                  row (m + ln sum exp(s - m)), or NULL to skip it. Must not
+ *                  overlap qkv or out.
+ *   softmax_scale  > 0 and finite (1/sqrt(128) for the model).
+ * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN, WAN_E_ALIAS,
+ * WAN_E_OVERFLOW, WAN_E_VALUE, WAN_E_HIP.
+ */
+int wan_attn_fwd(const void *qkv, void *out, float *lse,
+                 int64_t B, int64_t S, int64_t heads, int64_t head_dim,
+                 float softmax_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAN_ATTN_H */

@@ -137,14 +137,24 @@ def qknorm_rope_ref(qkv, gamma_q, gamma_k, grid, heads, head_dim,
         raise ValueError("S must equal T*H*W")
     D = heads * head_dim
     flat = qkv.reshape(B * S, 3 * D)
-    if rows is None:
-        rows = np.arange(B * S)
-    rows = np.asarray(rows)
-    tok = rows % S
+    rows = np.arange(B * S) if rows is None else np.asarray(rows)
+    out = qknorm_rope_tokens_ref(flat[rows], rows % S, gamma_q, gamma_k, grid, heads, head_dim, eps, theta)
+    out["rows"] = rows
+    return out
+
+
+def qknorm_rope_tokens_ref(x_rows, tokens, gamma_q, gamma_k, grid, heads, head_dim,
+                           eps=RMS_EPS, theta=ROPE_THETA):
+    """The same step for a set of packed rows given directly: x_rows [N, 3D]
+    (bf16 values) are the rows of tokens ``tokens`` (sequence index s of the
+    T x H x W grid). Returns the dict described in ``qknorm_rope_ref``."""
+    T, H, W = grid
+    D = heads * head_dim
+    tok = np.asarray(tokens)
     f, y, w = tok // (H * W), (tok // W) % H, tok % W
     out = {}
     for name, off, gamma in (("q", 0, gamma_q), ("k", D, gamma_k)):
-        x = flat[rows, off:off + D].astype(np.float64)
+        x = np.asarray(x_rows[:, off:off + D], dtype=np.float64)
         ms = np.mean(x * x, axis=-1, keepdims=True)  # over all heads of the token
         pre = x / np.sqrt(ms + eps) * np.asarray(gamma, np.float64)[None, :]
         n = bf16_rne(pre)
@@ -154,7 +164,6 @@ def qknorm_rope_ref(qkv, gamma_q, gamma_k, grid, heads, head_dim,
         out["n_" + name] = n
         out["out64_" + name] = rot
         out["out16_" + name] = bf16_rne(rot)
-    out["rows"] = rows
     return out
 
 

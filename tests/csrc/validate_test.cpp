@@ -1,0 +1,79 @@
+// Host-only test of the C-ABI argument validation (no HIP calls): every error
+// path returns its status before any memory is touched.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "validate.hpp"
+
+static int failures = 0;
+#define EXPECT_EQ(a, b)                                                                   \
+  do {                                                                                    \
+    long long _a = (a), _b = (b);                                                         \
+    if (_a != _b) {                                                                       \
+      std::fprintf(stderr, "%s:%d: %s = %lld, expected %lld\n", __FILE__, __LINE__, #a, _a, _b); \
+      ++failures;                                                                         \
+    }                                                                                     \
+  } while (0)
+
+int main() {
+  using namespace wan;
+  alignas(16) static unsigned char buf[1 << 20];
+  void* qkv = buf;                 // 1 MB fake "device" region (never dereferenced)
+  void* g1 = buf + 4096;  // inside the 196 KB packed buffer of the first call
+  void* g2 = buf + 8192;
+  Sizes z;
+  // norm + rope
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_E_ALIAS);  // gammas inside qkv range
+  static unsigned char other[8192] __attribute__((aligned(16)));
+  g1 = other;
+  g2 = other + 1024;
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_OK);
+  EXPECT_EQ(z.S, 128);
+  EXPECT_EQ(z.D, 256);
+  EXPECT_EQ(validate_qknorm_rope(nullptr, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_qknorm_rope(qkv, nullptr, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 2, 64, 1e-6f, 1e4f, &z), WAN_E_UNSUPPORTED);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 0, 128, 1e-6f, 1e4f, &z), WAN_E_SHAPE);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 257, 128, 1e-6f, 1e4f, &z), WAN_E_UNSUPPORTED);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, -1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_E_SHAPE);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, -2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_E_SHAPE);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 2, 128, -1.f, 1e4f, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 0.f, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 2, 128, NAN, 1e4f, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_qknorm_rope(buf + 2, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_E_ALIGN);
+  EXPECT_EQ(validate_qknorm_rope(qkv, other + 8, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_E_ALIGN);
+  // empty: OK without looking at pointers
+  EXPECT_EQ(validate_qknorm_rope(nullptr, nullptr, nullptr, 0, 2, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_OK);
+  EXPECT_EQ(z.empty, 1);
+  EXPECT_EQ(validate_qknorm_rope(nullptr, nullptr, nullptr, 1, 0, 8, 8, 2, 128, 1e-6f, 1e4f, &z), WAN_OK);
+  // overflow: S beyond 2^31-1, and B*S*3D beyond int64
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 1 << 20, 1 << 12, 1, 2, 128, 1e-6f, 1e4f, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, INT64_MAX / 2, 4, 1, 2, 128, 1e-6f, 1e4f, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, INT64_MAX / 1000, 1000, 1000, 1, 2, 128, 1e-6f, 1e4f, &z), WAN_E_OVERFLOW);
+
+  // attention
+  alignas(16) static unsigned char outb[1 << 16];
+  alignas(16) static float lseb[1024];
+  EXPECT_EQ(validate_attn(qkv, outb, lseb, 1, 16, 2, 128, 0.088f, 2, &z), WAN_OK);
+  EXPECT_EQ(validate_attn(qkv, outb, nullptr, 1, 16, 2, 128, 0.088f, 2, &z), WAN_OK);
+  EXPECT_EQ(validate_attn(qkv, nullptr, nullptr, 1, 16, 2, 128, 0.088f, 2, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_attn(qkv, buf + 4096, nullptr, 1, 16, 2, 128, 0.088f, 2, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn(qkv, outb, reinterpret_cast<float*>(outb + 16), 1, 16, 2, 128, 0.088f, 2, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn(qkv, outb, reinterpret_cast<float*>(buf + 64), 1, 16, 2, 128, 0.088f, 2, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn(qkv, outb + 8, nullptr, 1, 16, 2, 128, 0.088f, 2, &z), WAN_E_ALIGN);
+  EXPECT_EQ(validate_attn(qkv, outb, reinterpret_cast<float*>(reinterpret_cast<char*>(lseb) + 2), 1, 16, 2, 128, 0.088f, 2, &z), WAN_E_ALIGN);
+  EXPECT_EQ(validate_attn(qkv, outb, nullptr, 1, 16, 2, 96, 0.088f, 2, &z), WAN_E_UNSUPPORTED);
+  EXPECT_EQ(validate_attn(qkv, outb, nullptr, 1, 16, 2, 128, 0.f, 2, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn(qkv, outb, nullptr, 1, 16, 2, 128, INFINITY, 2, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn(nullptr, nullptr, nullptr, 3, 0, 2, 128, 0.088f, 2, &z), WAN_OK);
+  EXPECT_EQ(validate_attn(qkv, outb, nullptr, 1, (int64_t)INT32_MAX + 1, 2, 128, 0.088f, 2, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_attn(qkv, outb, nullptr, -2, 16, 2, 128, 0.088f, 2, &z), WAN_E_SHAPE);
+
+  if (failures) {
+    std::fprintf(stderr, "%d failures\n", failures);
+    return 1;
+  }
+  std::printf("validate_test: all checks passed\n");
+  return 0;
+}

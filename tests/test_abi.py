@@ -1,0 +1,70 @@
+"""CPU checks of the boundary: the built library loads and exports every
+symbol the header declares, the argument validation rejects every bad call
+before touching memory (host-only C++ test), and the host-side token-grid
+helper matches the pages' worked examples."""
+
+import ctypes
+import json
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wan_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(wan_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("wan_qknorm_rope", "wan_attn_fwd", "wan_status_str", "wan_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from video_diffusion_transformer_amd import wan_attn
+    if not os.path.exists(wan_attn.LIB_PATH):
+        pytest.skip("library not built")
+    lib = ctypes.CDLL(wan_attn.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(wan_attn.SIGNATURES), "binding and header disagree"
+    lib.wan_abi_version.restype = ctypes.c_int
+    assert lib.wan_abi_version() == 1
+    lib.wan_status_str.restype = ctypes.c_char_p
+    assert lib.wan_status_str(-5) == b"an output overlaps an input"
+
+
+def test_validation_rejects_bad_calls_host_only(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = tmp_path / "validate_test"
+    src = os.path.join(ROOT, "tests", "csrc", "validate_test.cpp")
+    subprocess.run([gxx, "-std=c++17", "-O1", "-Wall", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc"), src, "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_binding_token_grid_matches_worked_examples():
+    from video_diffusion_transformer_amd.wan_attn import token_grid
+    for c in json.load(open(os.path.join(ROOT, "tests", "golden", "output_spec.json")))["cases"]:
+        assert token_grid(c["width"], c["height"], c["frames"]) == (c["T"], c["H"], c["W"])
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from video_diffusion_transformer_amd import wan_attn
+    x = torch.zeros((1, 4, 768), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        wan_attn.attn_fwd(x, 2)
+    with pytest.raises(ValueError):
+        wan_attn.qknorm_rope(x, x[0, 0, :256], x[0, 0, :256], (1, 2, 2), 2)

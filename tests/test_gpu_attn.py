@@ -1,0 +1,152 @@
+"""GPU parity of wan_attn_fwd (through the C ABI) against the fp64 oracle.
+
+Inputs are the seeded synthetic packed buffers (N(0, 1) bf16 draws, whose
+score statistics match post-norm activations: unit-RMS q and k give
+q.k/sqrt(128) ~ N(0, 1)). Small shapes are compared in full; the full workload
+shapes on sampled query rows against all keys. The end-to-end test chains the
+norm step and attention on both sides.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import wan_ref
+from tests.parity import BF16_GATES, LSE_ABS, assert_gates, attn_error_stats, sample_rows
+from video_diffusion_transformer_amd import synth, wan_attn
+from video_diffusion_transformer_amd.configs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SCALE = 1.0 / math.sqrt(128.0)
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _full_compare(qkv, heads, what):
+    out, lse = wan_attn.attn_fwd(qkv.to(DEV), heads, lse=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = wan_ref.attn_packed_ref(_np(qkv), heads, 128, SCALE)
+    st = attn_error_stats(_np(out), o_ref)
+    assert_gates(st, BF16_GATES, what)
+    assert np.abs(_np(lse) - l_ref).max() <= LSE_ABS, what
+    return out
+
+
+def test_tiny_config():
+    w = WORKLOADS["tiny"]
+    _full_compare(synth.make_qkv(w.B, w.S, w.heads, seed=w.seed), w.heads, "tiny")
+
+
+@pytest.mark.parametrize("B,S,heads", [(1, 1, 1), (1, 105, 2), (1, 129, 1), (2, 200, 3), (1, 64, 2),
+                                       (1, 127, 1), (2, 300, 40), (1, 1000, 2)])
+def test_ragged_shapes(B, S, heads):
+    _full_compare(synth.make_qkv(B, S, heads, seed=S + heads), heads, f"B{B} S{S} h{heads}")
+
+
+def test_peaky_softmax_rescales():
+    """Q x 8 makes the softmax nearly one-hot and forces the running max to
+    move between tiles."""
+    qkv = synth.make_qkv(1, 500, 2, seed=11).float()
+    qkv[..., :256] *= 8
+    _full_compare(qkv.to(torch.bfloat16), 2, "peaky")
+
+
+def test_closed_forms():
+    heads, S = 2, 333
+    D = heads * 128
+    qkv = synth.make_qkv(1, S, heads, seed=12).float()
+    # Q = 0: uniform weights, O = mean(V), lse = ln S
+    z = qkv.clone()
+    z[..., :D] = 0
+    out, lse = wan_attn.attn_fwd(z.to(torch.bfloat16).to(DEV), heads, lse=True)
+    v = z[..., 2 * D:].to(torch.bfloat16).double()
+    ref = v.mean(dim=1, keepdim=True).expand(1, S, D)
+    assert (out.double().cpu() - ref).abs().max() <= 2e-3
+    assert (lse.double().cpu() - math.log(S)).abs().max() <= 1e-4
+    # V = constant: O = that constant
+    c = qkv.clone()
+    c[..., 2 * D:] = -1.75
+    out = wan_attn.attn_fwd(c.to(torch.bfloat16).to(DEV), heads)
+    assert (out.double().cpu() + 1.75).abs().max() <= 1e-2
+
+
+def test_deterministic_and_layout_independent():
+    """Same values at a different address (a separately assembled packed
+    buffer, offset inside a larger allocation) give bit-identical output; so do
+    repeated calls."""
+    B, S, heads = 1, 777, 2
+    D = heads * 128
+    qkv = synth.make_qkv(B, S, heads, seed=13).to(DEV)
+    a = wan_attn.attn_fwd(qkv, heads)
+    b = wan_attn.attn_fwd(qkv, heads)
+    q, k, v = qkv[..., :D].clone(), qkv[..., D:2 * D].clone(), qkv[..., 2 * D:].clone()
+    big = torch.empty(B * S * 3 * D + 64, dtype=torch.bfloat16, device=DEV)
+    other = big[64:].view(B, S, 3 * D)
+    other.copy_(torch.cat([q, k, v], dim=-1))
+    c = wan_attn.attn_fwd(other, heads)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_errors_and_empty():
+    qkv = torch.zeros((1, 16, 768), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(wan_attn.WanError) as e:
+        wan_attn.attn_fwd(qkv, 2, out=qkv[..., :256].contiguous().view(1, 16, 256), softmax_scale=-1.0)
+    assert e.value.status == -9
+    out = wan_attn.attn_fwd(torch.empty((0, 16, 768), dtype=torch.bfloat16, device=DEV), 2)
+    assert out.shape == (0, 16, 256)
+    with pytest.raises(wan_attn.WanError) as e:  # output inside the input
+        wan_attn.attn_fwd(qkv, 2, out=qkv.view(-1)[:16 * 256].view(1, 16, 256))
+    assert e.value.status == -5
+
+
+def test_end_to_end_norm_rope_then_attention():
+    """Both sides run the whole step from the same raw buffer."""
+    B, grid, heads = 2, (3, 6, 10), 4
+    S = grid[0] * grid[1] * grid[2]
+    D = heads * 128
+    qkv = synth.make_qkv(B, S, heads, seed=21)
+    gq, gk = synth.make_gammas(D, seed=21)
+    d = qkv.to(DEV)
+    wan_attn.qknorm_rope(d, gq.to(DEV), gk.to(DEV), grid, heads)
+    out, lse = wan_attn.attn_fwd(d, heads, lse=True)
+    torch.cuda.synchronize()
+    host = _np(qkv)
+    r = wan_ref.qknorm_rope_ref(host, _np(gq), _np(gk), grid, heads, 128)
+    normed = host.copy().reshape(B * S, 3 * D)
+    normed[:, :D] = r["out16_q"]
+    normed[:, D:2 * D] = r["out16_k"]
+    o_ref, l_ref = wan_ref.attn_packed_ref(normed.reshape(B, S, 3 * D), heads, 128, SCALE)
+    assert_gates(attn_error_stats(_np(out), o_ref), BF16_GATES, "end-to-end")
+    assert np.abs(_np(lse) - l_ref).max() <= LSE_ABS
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "long"])
+def test_full_size_sampled_rows(name):
+    """Full workload shape, same launch as the benchmark; ~64 seeded query rows
+    per (b, h) plus edge rows, each against all keys."""
+    w = WORKLOADS[name]
+    qkv = synth.make_qkv(w.B, w.S, w.heads, seed=w.seed, device=DEV)
+    out, lse = wan_attn.attn_fwd(qkv, w.heads, lse=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.S, 64, seed=w.seed, hw=w.H * w.W)
+    assert rows.min() >= 0 and rows.max() < w.S  # host-side bounds check before the GPU gather
+    rows_t = torch.from_numpy(rows).to(DEV)
+    got = _np(out.index_select(1, rows_t))
+    got_lse = _np(lse.index_select(2, rows_t))
+    heads_to_check = sorted({0, 1, w.heads // 2, w.heads - 1})
+    for b in range(w.B):
+        for h in heads_to_check:
+            c = slice(h * 128, (h + 1) * 128)
+            q = _np(qkv[b, :, h * 128:(h + 1) * 128].index_select(0, rows_t))
+            k = _np(qkv[b, :, w.D + h * 128:w.D + (h + 1) * 128])
+            v = _np(qkv[b, :, 2 * w.D + h * 128:2 * w.D + (h + 1) * 128])
+            o_ref, l_ref = wan_ref.attention_ref(q, k, v, SCALE)
+            assert_gates(attn_error_stats(got[b, :, c], o_ref), BF16_GATES, f"{name} b{b} h{h}")
+            assert np.abs(got_lse[b, h] - l_ref).max() <= LSE_ABS

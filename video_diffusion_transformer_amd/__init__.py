@@ -1,0 +1,9 @@
+"""MI355X-native (gfx950) hot path of one Wan2.2 DiT self-attention step.
+
+The computation lives in libwan_attn.so (hand-written HIP kernels behind the
+C ABI in include/wan_attn.h); this package holds the ctypes binding, the build
+script, the workload definitions and the seeded input generators.
+"""
+
+from .wan_attn import (WanError, attn_fwd, lib, qknorm_rope, token_grid)  # noqa: F401
+from .configs import WORKLOADS, Workload  # noqa: F401

@@ -1,0 +1,120 @@
+// extern "C" entry points of libwan_attn.so: validate -> (tables) -> launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "kernels.hpp"
+#include "validate.hpp"
+#include "wan_attn.h"
+
+namespace {
+
+// ---------------------------------------------------------------- RoPE tables
+// fp32 (cos, sin) of pos * theta^(-2j/d_a) for the frame axis (d_a = 44, 22
+// pairs), the row axis (42, 21 pairs) and the column axis (42, 21 pairs) --
+// Wan2.2's 3-D rotary split of a 128-channel head -- computed in double on the
+// host and rounded once to fp32. One device allocation per (device, T, H, W,
+// theta), kept until the process ends.
+using TabKey = std::tuple<int, int64_t, int64_t, int64_t, uint32_t>;
+std::mutex g_tab_mu;
+std::map<TabKey, float2*> g_tabs;
+
+int rope_table(int64_t T, int64_t H, int64_t W, float theta, const float2** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return WAN_E_HIP;
+  uint32_t tbits;
+  std::memcpy(&tbits, &theta, 4);
+  const TabKey key{dev, T, H, W, tbits};
+  std::lock_guard<std::mutex> lock(g_tab_mu);
+  auto it = g_tabs.find(key);
+  if (it != g_tabs.end()) {
+    *out = it->second;
+    return WAN_OK;
+  }
+  const int npairs[3] = {22, 21, 21};
+  const int64_t len[3] = {T, H, W};
+  std::vector<float2> host;
+  host.reserve(static_cast<size_t>(T * 22 + H * 21 + W * 21));
+  for (int a = 0; a < 3; ++a) {
+    const double da = 2.0 * npairs[a];
+    for (int64_t pos = 0; pos < len[a]; ++pos)
+      for (int j = 0; j < npairs[a]; ++j) {
+        const double omega = std::pow(static_cast<double>(theta), -2.0 * j / da);
+        const double phi = static_cast<double>(pos) * omega;
+        host.push_back(make_float2(static_cast<float>(std::cos(phi)), static_cast<float>(std::sin(phi))));
+      }
+  }
+  float2* dptr = nullptr;
+  if (hipMalloc(&dptr, host.size() * sizeof(float2)) != hipSuccess) return WAN_E_NOMEM;
+  if (hipMemcpy(dptr, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dptr);
+    return WAN_E_HIP;
+  }
+  g_tabs.emplace(key, dptr);
+  *out = dptr;
+  return WAN_OK;
+}
+
+constexpr int64_t kMaxRowsPerLaunch = 1 << 21;  // rows * threads per launch stays below 2^32
+
+}  // namespace
+
+extern "C" {
+
+int wan_abi_version(void) { return WAN_ABI_VERSION; }
+
+const char* wan_status_str(int status) {
+  switch (status) {
+    case WAN_OK: return "ok";
+    case WAN_E_NULL: return "a required pointer is NULL";
+    case WAN_E_SHAPE: return "invalid size (negative, zero where it must not be, or inconsistent)";
+    case WAN_E_UNSUPPORTED: return "unsupported configuration (head_dim must be 128, heads 1..256)";
+    case WAN_E_ALIGN: return "a pointer is not aligned as required (16 bytes; 4 for fp32 vectors)";
+    case WAN_E_ALIAS: return "an output overlaps an input";
+    case WAN_E_OVERFLOW: return "a size product overflows, or S exceeds 2^31-1";
+    case WAN_E_HIP: return "HIP runtime error or kernel launch failure";
+    case WAN_E_NOMEM: return "device allocation of a library table failed";
+    case WAN_E_VALUE: return "a scalar argument is out of range";
+    default: return "unknown status";
+  }
+}
+
+int wan_qknorm_rope(void* qkv, const void* gamma_q, const void* gamma_k, int64_t B, int64_t T,
+                    int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
+                    void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_qknorm_rope(qkv, gamma_q, gamma_k, B, T, H, W, heads, head_dim, eps, theta, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (T > INT32_MAX / 22 || H > INT32_MAX / 21 || W > INT32_MAX / 21) return WAN_E_OVERFLOW;
+  const float2* tab = nullptr;
+  rc = rope_table(T, H, W, theta, &tab);
+  if (rc != WAN_OK) return rc;
+  auto st = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < z.rows; r0 += kMaxRowsPerLaunch) {
+    const int64_t n = z.rows - r0 < kMaxRowsPerLaunch ? z.rows - r0 : kMaxRowsPerLaunch;
+    if (wan::launch_qknorm_rope(qkv, gamma_q, gamma_k, tab, r0, n, static_cast<int>(z.S), static_cast<int>(T),
+                                static_cast<int>(H), static_cast<int>(W), static_cast<int>(z.D), eps,
+                                st) != hipSuccess)
+      return WAN_E_HIP;
+  }
+  return WAN_OK;
+}
+
+int wan_attn_fwd(const void* qkv, void* out, float* lse, int64_t B, int64_t S, int64_t heads,
+                 int64_t head_dim, float softmax_scale, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_attn(qkv, out, lse, B, S, heads, head_dim, softmax_scale, 2, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (B > INT32_MAX) return WAN_E_OVERFLOW;
+  if (wan::launch_attn_fwd(qkv, out, lse, static_cast<int>(B), static_cast<int>(S), static_cast<int>(heads),
+                           softmax_scale, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
+}  // extern "C"

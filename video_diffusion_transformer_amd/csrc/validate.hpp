@@ -1,0 +1,106 @@
+// Argument validation of the C ABI. Pure C++ (no HIP types or calls), so the
+// same checks compile into the library and into a host-only test program.
+//
+// Every entry point validates before it touches memory or the HIP runtime, and
+// returns a negative wan_status on the first failed check. The preconditions
+// mirror the ones the TensorRT-LLM pull request "Optimize Wan2.2 Dataflow"
+// lists for its packed QKV path (section "Fallback Behavior": self-attention,
+// fused QKV, bf16 Q and K, matching head dims, rotary embeddings available,
+// compatible norm weights) -- except that an unsupported case is an error here,
+// never a silent fallback (the vLLM-Omni "Wan2.2 Text-to-Video" recipe, Notes:
+// raise rather than degrade).
+#pragma once
+
+#include <cmath>
+#include <cstdint>
+
+#include "wan_attn.h"
+
+namespace wan {
+
+constexpr int64_t kHeadDim = 128;
+constexpr int64_t kMaxHeads = 256;
+constexpr int64_t kMaxTokens = INT32_MAX;  // token indices are 32-bit inside the kernels
+
+// a*b with overflow detection for non-negative operands.
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
+inline bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
+struct Sizes {
+  int64_t B = 0, S = 0, heads = 0, D = 0;
+  int64_t rows = 0;       // B*S
+  int64_t qkv_elems = 0;  // B*S*3D
+  int64_t out_elems = 0;  // B*S*D
+  bool empty = false;
+};
+
+// Shared shape checks. Returns WAN_OK and fills `z`, or an error.
+inline int check_sizes(int64_t B, int64_t S, int64_t heads, int64_t head_dim, Sizes* z) {
+  if (B < 0 || S < 0) return WAN_E_SHAPE;
+  if (head_dim != kHeadDim) return WAN_E_UNSUPPORTED;
+  if (heads < 1 || heads > kMaxHeads) return heads < 1 ? WAN_E_SHAPE : WAN_E_UNSUPPORTED;
+  if (S > kMaxTokens) return WAN_E_OVERFLOW;
+  z->B = B;
+  z->S = S;
+  z->heads = heads;
+  z->D = heads * head_dim;
+  if (!mul_ok(B, S, &z->rows)) return WAN_E_OVERFLOW;
+  int64_t t;
+  if (!mul_ok(z->rows, 3 * z->D, &z->qkv_elems)) return WAN_E_OVERFLOW;
+  if (!mul_ok(z->qkv_elems, 2, &t)) return WAN_E_OVERFLOW;  // bytes
+  if (!mul_ok(z->rows, z->D, &z->out_elems)) return WAN_E_OVERFLOW;
+  int64_t lse_elems;
+  if (!mul_ok(B * heads, S, &lse_elems)) return WAN_E_OVERFLOW;
+  z->empty = (z->rows == 0);
+  return WAN_OK;
+}
+
+inline int validate_qknorm_rope(const void* qkv, const void* gq, const void* gk, int64_t B, int64_t T,
+                                int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps,
+                                float theta, Sizes* z) {
+  if (T < 0 || H < 0 || W < 0) return WAN_E_SHAPE;
+  int64_t hw, S;
+  if (!mul_ok(H, W, &hw) || !mul_ok(hw, T, &S)) return WAN_E_OVERFLOW;
+  int rc = check_sizes(B, S, heads, head_dim, z);
+  if (rc != WAN_OK) return rc;
+  if (!std::isfinite(eps) || eps < 0.f) return WAN_E_VALUE;
+  if (!std::isfinite(theta) || theta <= 0.f) return WAN_E_VALUE;
+  if (z->empty) return WAN_OK;
+  if (!qkv || !gq || !gk) return WAN_E_NULL;
+  if (!aligned(qkv, 16) || !aligned(gq, 16) || !aligned(gk, 16)) return WAN_E_ALIGN;
+  const int64_t qkv_bytes = z->qkv_elems * 2, g_bytes = z->D * 2;
+  if (overlaps(qkv, qkv_bytes, gq, g_bytes) || overlaps(qkv, qkv_bytes, gk, g_bytes)) return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
+inline int validate_attn(const void* qkv, const void* out, const void* lse, int64_t B, int64_t S,
+                         int64_t heads, int64_t head_dim, float scale, int64_t in_elem_bytes,
+                         Sizes* z) {
+  int rc = check_sizes(B, S, heads, head_dim, z);
+  if (rc != WAN_OK) return rc;
+  if (!std::isfinite(scale) || scale <= 0.f) return WAN_E_VALUE;
+  if (z->empty) return WAN_OK;
+  if (!qkv || !out) return WAN_E_NULL;
+  if (!aligned(qkv, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return WAN_E_ALIGN;
+  const int64_t in_bytes = z->qkv_elems * in_elem_bytes, out_bytes = z->out_elems * 2;
+  const int64_t lse_bytes = z->B * z->heads * z->S * 4;
+  if (overlaps(qkv, in_bytes, out, out_bytes)) return WAN_E_ALIAS;
+  if (lse && (overlaps(lse, lse_bytes, qkv, in_bytes) || overlaps(lse, lse_bytes, out, out_bytes)))
+    return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
+}  // namespace wan

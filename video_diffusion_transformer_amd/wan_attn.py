@@ -1,0 +1,147 @@
+"""Python binding of libwan_attn.so (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/wan_attn.h. Tensors must already
+live on the GPU; there is no CPU path. If the library is not built the first
+call raises -- nothing falls back to another implementation.
+
+The names follow the C ABI: ``qknorm_rope`` -> wan_qknorm_rope,
+``attn_fwd`` -> wan_attn_fwd.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwan_attn.so")
+
+HEAD_DIM = 128
+RMS_EPS = 1e-6
+ROPE_THETA = 10000.0
+
+_STATUS = {
+    0: "WAN_OK", -1: "WAN_E_NULL", -2: "WAN_E_SHAPE", -3: "WAN_E_UNSUPPORTED", -4: "WAN_E_ALIGN",
+    -5: "WAN_E_ALIAS", -6: "WAN_E_OVERFLOW", -7: "WAN_E_HIP", -8: "WAN_E_NOMEM", -9: "WAN_E_VALUE",
+}
+
+# (name, restype, argtypes) of every symbol the header declares.
+_P, _I64, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+SIGNATURES = {
+    "wan_abi_version": (ctypes.c_int, []),
+    "wan_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
+    "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
+}
+
+
+class WanError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m video_diffusion_transformer_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise WanError(fn, status, lib().wan_status_str(status).decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need_gpu(name, t, dtype):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def token_grid(width, height, num_frames):
+    """(T, H, W) token grid of a clip: height and width rounded down to a
+    multiple of 16, 8x spatial / 4x temporal VAE compression, 2x2 patchify
+    ("Optimizing High-Quality Offline Video Generation", Grounding in an output
+    spec)."""
+    if num_frames < 1 or (num_frames - 1) % 4:
+        raise ValueError("num_frames must be 4k+1")
+    w = (width // 16) * 16 // 8 // 2
+    h = (height // 16) * 16 // 8 // 2
+    return (num_frames - 1) // 4 + 1, h, w
+
+
+def qknorm_rope(qkv, gamma_q, gamma_k, grid, heads, head_dim=HEAD_DIM, eps=RMS_EPS,
+                theta=ROPE_THETA, stream=None):
+    """In-place Q/K RMSNorm + bf16 rounding + 3-D RoPE on a packed
+    [B, S, 3*heads*head_dim] bf16 tensor (S = T*H*W). Returns qkv."""
+    T, H, W = grid
+    _need_gpu("qkv", qkv, torch.bfloat16)
+    _need_gpu("gamma_q", gamma_q, torch.bfloat16)
+    _need_gpu("gamma_k", gamma_k, torch.bfloat16)
+    B = qkv.shape[0]
+    D = heads * head_dim
+    if qkv.dim() != 3 or qkv.shape[1] != T * H * W or qkv.shape[2] != 3 * D:
+        raise ValueError(f"qkv must be [B, {T * H * W}, {3 * D}], got {tuple(qkv.shape)}")
+    if gamma_q.numel() != D or gamma_k.numel() != D:
+        raise ValueError("gammas must have heads*head_dim elements")
+    with torch.cuda.device(qkv.device):
+        _check("wan_qknorm_rope", lib().wan_qknorm_rope(
+            _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), B, T, H, W, heads, head_dim, eps, theta,
+            _stream(qkv.device, stream)))
+    return qkv
+
+
+def attn_fwd(qkv, heads, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=False, stream=None):
+    """Bidirectional attention over a packed bf16 [B, S, 3*D] tensor.
+    Returns out [B, S, D] bf16, or (out, lse [B, heads, S] fp32) when lse is
+    True or a preallocated tensor."""
+    _need_gpu("qkv", qkv, torch.bfloat16)
+    B, S = qkv.shape[0], qkv.shape[1]
+    D = heads * head_dim
+    if qkv.dim() != 3 or qkv.shape[2] != 3 * D:
+        raise ValueError(f"qkv must be [B, S, {3 * D}], got {tuple(qkv.shape)}")
+    scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=qkv.device)
+    _need_gpu("out", out, torch.bfloat16)
+    if tuple(out.shape) != (B, S, D):
+        raise ValueError("out must be [B, S, D]")
+    want_lse = lse is not False and lse is not None
+    if lse is True:
+        lse = torch.empty((B, heads, S), dtype=torch.float32, device=qkv.device)
+    if want_lse:
+        _need_gpu("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, heads, S):
+            raise ValueError("lse must be [B, heads, S]")
+    with torch.cuda.device(qkv.device):
+        _check("wan_attn_fwd", lib().wan_attn_fwd(
+            _ptr(qkv), _ptr(out), _ptr(lse) if want_lse else ctypes.c_void_p(0), B, S, heads,
+            head_dim, scale, _stream(qkv.device, stream)))
+    return (out, lse) if want_lse else out
