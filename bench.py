@@ -110,9 +110,7 @@ def main():
     out = torch.empty((w.B, w.S, w.D), dtype=torch.bfloat16, device=dev)
     fp8 = w.dtype == "fp8"
     if fp8:
-        qkv8 = torch.empty((w.B, w.S, 3 * w.D), dtype=torch.uint8, device=dev)
-        scales = torch.empty(3, dtype=torch.float32, device=dev)
-        amax = torch.empty(3, dtype=torch.float32, device=dev)
+        f8 = wan_attn.fp8_buffers(w.B, w.S, w.heads, dev)
     stream = torch.cuda.current_stream(dev)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -121,9 +119,9 @@ def main():
         wan_attn.qknorm_rope(qkv, gq, gk, grid, w.heads)
         if ev: ev[1].record(stream)
         if fp8:
-            wan_attn.qkv_quant_fp8(qkv, w.heads, out=qkv8, scales=scales, amax=amax)
+            wan_attn.qkv_quant_fp8(qkv, w.heads, out=f8)
             if ev: ev[2].record(stream)
-            wan_attn.attn_fwd_fp8(qkv8, scales, w.heads, out=out)
+            wan_attn.attn_fwd_fp8(f8, out=out)
         else:
             if ev: ev[2].record(stream)
             wan_attn.attn_fwd(qkv, w.heads, out=out)

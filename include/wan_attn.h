@@ -144,6 +144,56 @@ int wan_attn_fwd(const void *qkv, void *out, float *lse,
                  int64_t B, int64_t S, int64_t heads, int64_t head_dim,
                  float softmax_scale, void *stream);
 
+/*
+ * wan_qkv_quant_fp8 -- per-tensor e4m3 quantisation of Q, K and V for the fp8
+ * attention path (the amax -> E4M3 scale -> quantise recipe of "Optimize Wan2.2
+ * Dataflow", change 2, applied to the attention inputs; the pull request's
+ * 720p attention itself runs in FP8).
+ *
+ * For X in (Q, K, V), over all B*S*D elements of X:
+ *   amax[X]   = max |x|
+ *   scale[X]  = 448 / amax[X] in fp32 (IEEE division), or 1 if amax is 0
+ *   x8        = e4m3( fl32(x * scale[X]) ), round to nearest even, saturated
+ *               to +-448 (OCP E4M3, the gfx950 fp8 format; never NaN)
+ *
+ *   qkv     bf16 [B, S, 3*D] packed buffer (normally after wan_qknorm_rope);
+ *           read only.
+ *   qk8     e4m3 [B, S, 2*D] output: per token Q (all heads) then K.
+ *   vt8     e4m3 [B, heads, 128, S_pad] output: V of each head transposed
+ *           (channel-major, keys contiguous), S_pad = S rounded up to 128;
+ *           positions S..S_pad-1 are written as 0. Size: wan_fp8_vt_bytes().
+ *   scales  device float[3] output: scale of Q, K, V (x8 = x * scale).
+ *   amax    device float[3] output: amax of Q, K, V (also used as the
+ *           reduction target; cleared by the call itself).
+ * Three kernels on `stream` (clear, amax, quantise). Outputs must not overlap
+ * each other or qkv. Calls that share `amax` must not overlap in time.
+ * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN (16-byte
+ * tensors, 4-byte scale vectors), WAN_E_ALIAS, WAN_E_OVERFLOW (also B > 65535),
+ * WAN_E_HIP.
+ */
+int wan_qkv_quant_fp8(const void *qkv, void *qk8, void *vt8, float *scales, float *amax,
+                      int64_t B, int64_t S, int64_t heads, int64_t head_dim, void *stream);
+
+/* Bytes of the vt8 buffer for (B, S, heads, head_dim); -1 on invalid sizes or
+ * overflow. Pure host arithmetic. */
+int64_t wan_fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim);
+
+/*
+ * wan_attn_fwd_fp8 -- bidirectional attention from the wan_qkv_quant_fp8
+ * buffers on fp8 MFMA (16x16x128 e4m3, fp32 accumulation):
+ *   s     = (q8 . k8) / (scale_q * scale_k) * softmax_scale      (fp32)
+ *   p     = softmax over all S keys (fp32, online)
+ *   out   = sum_t e4m3(p * 2^8) v8 / (2^8 * scale_v * l),  l = fp32 sum of p
+ *
+ *   qk8, vt8, scales  as written by wan_qkv_quant_fp8 for the same sizes.
+ *   out               bf16 [B, S, D]; must not overlap the inputs.
+ *   lse               fp32 [B, heads, S] natural log-sum-exp of the scores, or NULL.
+ * Errors: as wan_attn_fwd.
+ */
+int wan_attn_fwd_fp8(const void *qk8, const void *vt8, const float *scales, void *out, float *lse,
+                     int64_t B, int64_t S, int64_t heads, int64_t head_dim, float softmax_scale,
+                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

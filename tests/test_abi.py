@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "wan_attn.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(wan_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int64_t|int|const char \*)\s*(wan_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():

@@ -1,0 +1,122 @@
+"""GPU parity of the fp8 path (wan_qkv_quant_fp8, wan_attn_fwd_fp8) against
+the oracle: amax and scales exact, every e4m3 byte bit-exact (the code decision
+is taken in fp32 on both sides), V transposed per head with zero padding, and
+the fp8 attention within the fp8 gates of the dequantised fp64 reference."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import wan_ref
+from tests.parity import FP8_GATES, LSE_ABS, assert_gates, attn_error_stats, sample_rows
+from video_diffusion_transformer_amd import synth, wan_attn
+from video_diffusion_transformer_amd.configs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SCALE = 1.0 / math.sqrt(128.0)
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _vt_view(f, heads):
+    return f.vt8.view(f.B, heads, 128, f.s_pad)
+
+
+def _check_quant(qkv, heads):
+    B, S = qkv.shape[0], qkv.shape[1]
+    D = heads * 128
+    f = wan_attn.qkv_quant_fp8(qkv.to(DEV), heads)
+    torch.cuda.synchronize()
+    r = wan_ref.quant_fp8_ref(_np(qkv), heads, 128)
+    np.testing.assert_array_equal(f.amax.cpu().numpy().astype(np.float64), r["amax"])
+    np.testing.assert_array_equal(f.scales.cpu().numpy().astype(np.float64), r["scale"])
+    codes = r["codes"]
+    np.testing.assert_array_equal(f.qk8.cpu().numpy(), codes[..., :2 * D])
+    vt = _vt_view(f, heads).cpu().numpy()
+    ref_vt = codes[..., 2 * D:].reshape(B, S, heads, 128).transpose(0, 2, 3, 1)
+    np.testing.assert_array_equal(vt[..., :S], ref_vt)
+    assert not vt[..., S:].any(), "padding past S must be zero"
+    return f, r
+
+
+@pytest.mark.parametrize("B,S,heads", [(1, 128, 2), (2, 200, 3), (1, 1, 1), (1, 300, 40)])
+def test_quant_bit_exact(B, S, heads):
+    _check_quant(synth.make_qkv(B, S, heads, seed=S + 7 * heads), heads)
+
+
+def test_quant_all_zero_and_outlier():
+    qkv = torch.zeros((1, 64, 768), dtype=torch.bfloat16)
+    qkv[0, 5, 300] = 1000.0   # one K outlier; Q and V all zero
+    f, r = _check_quant(qkv, 2)
+    assert list(f.scales.cpu().numpy()) == [1.0, float(np.float32(448.0) / np.float32(1000.0)), 1.0]
+
+
+def _check_attn(qkv, heads, what, rows=None):
+    f, r = _check_quant(qkv, heads) if rows is None else (wan_attn.qkv_quant_fp8(qkv.to(DEV), heads), None)
+    out, lse = wan_attn.attn_fwd_fp8(f, lse=True)
+    torch.cuda.synchronize()
+    deq = r["deq"]
+    o_ref, l_ref = wan_ref.attn_packed_ref(deq, heads, 128, SCALE)
+    st = attn_error_stats(_np(out), o_ref)
+    assert_gates(st, FP8_GATES, what)
+    assert np.abs(_np(lse) - l_ref).max() <= 5e-2, what
+    return st
+
+
+def test_tiny_fp8_attention():
+    w = WORKLOADS["tiny"]
+    _check_attn(synth.make_qkv(w.B, w.S, w.heads, seed=w.seed), w.heads, "tiny fp8")
+
+
+@pytest.mark.parametrize("B,S,heads", [(1, 1, 1), (1, 129, 2), (2, 333, 3), (1, 1000, 2), (2, 256, 40)])
+def test_ragged_fp8_attention(B, S, heads):
+    _check_attn(synth.make_qkv(B, S, heads, seed=3 * S + heads), heads, f"fp8 B{B} S{S} h{heads}")
+
+
+def test_peaky_fp8_attention():
+    qkv = synth.make_qkv(1, 700, 2, seed=5).float()
+    qkv[..., :256] *= 6
+    _check_attn(qkv.to(torch.bfloat16), 2, "fp8 peaky")
+
+
+def test_fp8_720p_sampled_rows():
+    """The fp8 workload: 720p shape, quantisation checked on sampled tokens,
+    attention on sampled query rows of four heads per batch entry."""
+    w = WORKLOADS["720p_fp8"]
+    qkv = synth.make_qkv(w.B, w.S, w.heads, seed=w.seed, device=DEV)
+    f = wan_attn.qkv_quant_fp8(qkv, w.heads)
+    out, lse = wan_attn.attn_fwd_fp8(f, lse=True)
+    torch.cuda.synchronize()
+    # exact amax / scales from the whole tensor (computed here with torch, a library reduction)
+    D = w.D
+    amax = [qkv[..., i * D:(i + 1) * D].abs().max().item() for i in range(3)]
+    np.testing.assert_array_equal(f.amax.cpu().numpy(), np.array(amax, np.float32))
+    scales = [wan_ref.fp8_scale(a) for a in amax]
+    np.testing.assert_array_equal(f.scales.cpu().numpy().astype(np.float64), scales)
+    rows = sample_rows(w.S, 48, seed=w.seed, hw=w.H * w.W)
+    assert rows.min() >= 0 and rows.max() < w.S
+    rows_t = torch.from_numpy(rows).to(DEV)
+    got = _np(out.index_select(1, rows_t))
+    got_lse = _np(lse.index_select(2, rows_t))
+    vt = _vt_view(f, w.heads)
+    for b in range(w.B):
+        for h in sorted({0, w.heads // 2, w.heads - 1}):
+            raw = _np(qkv[b])
+            q = raw[rows, h * 128:(h + 1) * 128]
+            k = raw[:, D + h * 128:D + (h + 1) * 128]
+            v = raw[:, 2 * D + h * 128:2 * D + (h + 1) * 128]
+            # oracle quantisation of this head's slices with the tensor-wide scales
+            from oracle.numerics import e4m3_rne_sat, f32, e4m3_encode
+            q8 = e4m3_rne_sat(f32(q * scales[0])) / scales[0]
+            k8 = e4m3_rne_sat(f32(k * scales[1])) / scales[1]
+            v8c = e4m3_rne_sat(f32(v * scales[2]))
+            np.testing.assert_array_equal(vt[b, h, :, :w.S].cpu().numpy().T, e4m3_encode(v8c))
+            o_ref, l_ref = wan_ref.attention_ref(q8, k8, v8c / scales[2], SCALE)
+            assert_gates(attn_error_stats(got[b, :, h * 128:(h + 1) * 128], o_ref), FP8_GATES, f"720p fp8 b{b} h{h}")
+            assert np.abs(got_lse[b, h] - l_ref).max() <= 5e-2

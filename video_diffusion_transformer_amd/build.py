@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwan_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "qknorm_rope.hip", "attn_fwd.hip"]
+SOURCES = ["api.cpp", "qknorm_rope.hip", "attn_fwd.hip", "quant_fp8.hip", "attn_fwd_fp8.hip"]
 
 
 def hipcc():
@@ -34,6 +34,7 @@ def hipcc():
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-fno-honor-nans",  # max/min need no NaN canonicalisation; NaN inputs give unspecified results
             "-Wall", "-Wno-unused-command-line-argument",
             "-I", INCLUDE, "-I", CSRC]
 

@@ -117,4 +117,33 @@ int wan_attn_fwd(const void* qkv, void* out, float* lse, int64_t B, int64_t S, i
   return WAN_OK;
 }
 
+int wan_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int64_t B, int64_t S,
+                      int64_t heads, int64_t head_dim, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_quant_fp8(qkv, qk8, vt8, scales, amax, B, S, heads, head_dim, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (wan::launch_qkv_quant_fp8(qkv, qk8, vt8, scales, amax, static_cast<int>(B), static_cast<int>(S),
+                                static_cast<int>(heads), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
+int64_t wan_fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim) {
+  if (B < 0 || S < 0 || heads < 0 || head_dim != wan::kHeadDim) return -1;
+  int64_t n;
+  return wan::fp8_vt_bytes(B, S, heads, &n) ? n : -1;
+}
+
+int wan_attn_fwd_fp8(const void* qk8, const void* vt8, const float* scales, void* out, float* lse, int64_t B,
+                     int64_t S, int64_t heads, int64_t head_dim, float softmax_scale, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_attn_fp8(qk8, vt8, scales, out, lse, B, S, heads, head_dim, softmax_scale, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (B > INT32_MAX) return WAN_E_OVERFLOW;
+  if (wan::launch_attn_fwd_fp8(qk8, vt8, scales, out, lse, static_cast<int>(B), static_cast<int>(S),
+                               static_cast<int>(heads), softmax_scale, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
 }  // extern "C"

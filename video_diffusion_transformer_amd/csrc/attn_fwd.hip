@@ -1,5 +1,5 @@
 // Bidirectional multi-head flash-attention forward on the packed [Q|K|V]
-// buffer, bf16 MFMA with fp32 accumulation (gfx950 v_mfma_f32_32x32x16_bf16).
+// buffer, bf16 MFMA with fp32 accumulation (gfx950 v_mfma_f32_16x16x32_bf16).
 //
 // What it computes: for every (batch, head) and every query row, softmax over
 // ALL keys of (q . k) * scale, times V -- the unmasked attention of the Wan2.2
@@ -8,19 +8,29 @@
 //
 // Work decomposition
 //   * one workgroup = 4 wavefronts = 128 query rows of one (b, h); each wave owns
-//     32 rows for the whole kernel;
-//   * keys stream in tiles of 64; each tile's K (row-major) and V (transposed to
-//     [channel][key]) are staged in LDS, the next tile is prefetched into
-//     registers while the current one is consumed;
-//   * scores are computed transposed, S^T = K Q^T, so that after the MFMA every
-//     lane holds 32 key scores of ONE query row: the running max / sum of the
-//     online softmax stay lane-local (one cross-lane max with the partner lane
-//     l^32 per tile), and the bf16 probabilities are already in the register
-//     layout of the B operand of O^T = V^T P^T. The K rows are fed to the MFMA
-//     in a permuted order (bits 2 and 3 of the row swapped) so that the
-//     accumulator's key order matches the operand's k order exactly;
-//   * the output accumulator O^T keeps one query column per lane, so the
-//     per-row rescale by exp2(m_old - m_new) is lane-local too;
+//     32 rows (two 16-row MFMA column tiles) for the whole kernel;
+//   * keys stream in units of 32 through a ring of four LDS stages. In the
+//     iteration that consumes unit j, the scores of unit j+1 are computed (MFMA)
+//     while the exponentials of unit j run (VALU), then PV of unit j; unit j+2,
+//     loaded into registers one iteration earlier, is written to the stage unit
+//     j-2 used, and one barrier per unit publishes it;
+//   * scores are computed transposed, S^T = K Q^T (16x16x32 MFMA: A = 16 keys x
+//     32 channels from LDS, B = Q held in registers), so after the MFMA each
+//     lane holds scores of ONE query column: the online-softmax max and sum are
+//     lane-local plus two cross-lane steps (lanes l^16, l^32 share the query);
+//   * the bf16 probabilities of two adjacent 16-key tiles are already the B
+//     operand of O^T = V^T P^T (lane group g holds keys 4g..4g+3 of each tile);
+//     the V^T A operand is read straight from the row-major V tile with the
+//     gfx950 transposing LDS load ds_read_b64_tr_b16 (inside each 16-lane group,
+//     lane i receives element i%4 of the 8 bytes lane 4j+i/4 addressed, so 16
+//     lanes addressing 4 key rows x 16 channels each receive one channel with
+//     its 4 keys), pointed at exactly those key rows;
+//   * the O^T accumulator keeps one query column per lane, so the rescale by
+//     exp2(m_old - m_new) is lane-local. The running max only moves when a
+//     tile's max exceeds it by more than 8 (log2 units): most tiles skip the
+//     rescale; the stale max keeps p <= 2^8 (exact in fp32, far from bf16
+//     overflow) and the final normalisation uses the same max, so the result is
+//     unchanged;
 //   * workgroups are numbered so that consecutive q-tiles of the same head land
 //     on the same XCD (blocks are dispatched round-robin over the 8 XCDs), and
 //     that XCD's L2 serves the head's K/V to all of them.
@@ -32,20 +42,24 @@ namespace wan {
 namespace {
 
 constexpr int kD = 128;                  // head dim
-constexpr int kBN = 64;                  // keys per tile
+constexpr int kBN = 32;                  // keys per pipeline unit
+constexpr int kStages = 4;               // LDS ring of K/V units
 constexpr int kWaves = 4;                // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;         // query rows per workgroup
-constexpr int kKPitch = kD * 2 + 16;     // bytes per K row in LDS (16 B pad: conflict-free b128 reads)
-constexpr int kVPitch = kBN * 2 + 16;    // bytes per V^T row in LDS
+#ifndef WAN_ATTN_KPAD
+#define WAN_ATTN_KPAD 16
+#endif
+#ifndef WAN_ATTN_VPAD
+#define WAN_ATTN_VPAD 32
+#endif
+constexpr int kKPitch = kD * 2 + WAN_ATTN_KPAD;  // K row pitch in LDS: 16 rows at distinct 4-bank offsets (b128 reads)
+constexpr int kVPitch = kD * 2 + WAN_ATTN_VPAD;  // V row pitch: 8 rows x 32 B tile the 64 banks (transposed b64 reads)
 constexpr int kKBytes = kBN * kKPitch;
-constexpr int kVBytes = kD * kVPitch;
-
-// Row of the 32-key sub-tile that the MFMA A-operand lane m must load so that
-// accumulator register 4g+r of lane l holds key 16*(g/2) + 8*(l/32) + 4*(g%2) + r.
-__device__ __forceinline__ int perm_row(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
+constexpr int kVBytes = kBN * kVPitch;
+constexpr int kStage = kKBytes + kVBytes;
+constexpr int kChunks = kBN * 16 / kThreads;  // 16-byte chunks of K (and of V) per thread per unit
+constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag behind the true max
 
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   const int xcd = bid & 7, j = bid >> 3;
@@ -53,173 +67,219 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd * q + (xcd < r ? xcd : r) + j;
 }
 
+__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, float* __restrict__ lse,
                 int S, int heads, int nqt, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kKBytes + kVBytes];
-  unsigned char* ks = smem;
-  unsigned char* vs = smem + kKBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStage];
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = lid % nqt;
   const int bh = lid / nqt;
   const int h = bh % heads, b = bh / heads;
   const int D = heads * kD;
-  const int64_t rs = 3 * (int64_t)D;  // row stride in elements
+  const int rs = 3 * D;  // row stride in elements (< 2^17)
   const uint16_t* base = qkv + (int64_t)b * S * rs + h * kD;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
+  const int l16 = lane & 15, grp = lane >> 4;
 
-  // Q fragment (B operand of S^T = K Q^T): query row l32 of this wave, channels 16k + 8*hi.
-  const int qrow = qt * kBM + wave * 32 + l32;
-  const int qrow_c = qrow < S ? qrow : S - 1;
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qp = base + (int64_t)qrow_c * rs + 8 * hi;
+  // Q fragments (B operand of S^T = K Q^T): query 16u + l16 of this wave,
+  // channels 32k + 8*grp .. +7.
+  const int q0 = qt * kBM + wave * 32;
+  bf16x8_t qf[2][4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qf[k] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * k);
+  for (int u = 0; u < 2; ++u) {
+    int q = q0 + 16 * u + l16;
+    q = q < S ? q : S - 1;
+    const uint16_t* qp = base + (int64_t)q * rs + 8 * grp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qf[u][k] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * k);
   }
 
-  f32x16_t acc_o[4];
+  f32x4_t acc_o[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc_o[i] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int i = 0; i < 8; ++i) acc_o[i][0] = acc_o[i][1] = f32x4_t{};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  // Global -> register staging of one K/V tile. K: 4 x 16 B per thread, key = c/16, chunk c%16.
-  // V: key = tid%64, channel group 8*(tid/64 + 4i).
-  u32x4_t kreg[4], vreg[4];
-  auto load_tile = [&](int k0) {
+  // Staging of one unit (32 keys) of K and V: chunk c = tid + 256 i -> key c/16,
+  // channels 8*(c%16). Offsets are 32-bit element offsets from the unit's first row.
+  int g_off[kChunks], sk_off[kChunks], sv_off[kChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kThreads;
-      int key = k0 + (c >> 4);
-      key = key < S ? key : S - 1;
-      kreg[i] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)key * rs + D + 8 * (c & 15));
-    }
-    int key = k0 + lane;
-    key = key < S ? key : S - 1;
-    const uint16_t* vp = base + (int64_t)key * rs + 2 * D;
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = tid + i * kThreads;
+    g_off[i] = (c >> 4) * rs + 8 * (c & 15);
+    sk_off[i] = (c >> 4) * kKPitch + (c & 15) * 16;
+    sv_off[i] = (c >> 4) * kVPitch + (c & 15) * 16;
+  }
+  u32x4_t kreg[kChunks], vreg[kChunks];
+  auto load_unit = [&](int k0) {
+    const uint16_t* ub = base + (int64_t)k0 * rs;
+    if (k0 + kBN <= S) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vreg[i] = *reinterpret_cast<const u32x4_t*>(vp + 8 * (wave + 4 * i));
-  };
-  auto store_tile = [&]() {
+      for (int i = 0; i < kChunks; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x4_t*>(ub + g_off[i] + D);
+        vreg[i] = *reinterpret_cast<const u32x4_t*>(ub + g_off[i] + 2 * D);
+      }
+    } else {  // ragged last unit: rows past the end re-read row S-1 (masked later)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kThreads;
-      *reinterpret_cast<u32x4_t*>(ks + (c >> 4) * kKPitch + (c & 15) * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = 8 * (wave + 4 * i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<uint16_t*>(vs + (d0 + 2 * j) * kVPitch + lane * 2) = static_cast<uint16_t>(vreg[i][j]);
-        *reinterpret_cast<uint16_t*>(vs + (d0 + 2 * j + 1) * kVPitch + lane * 2) = static_cast<uint16_t>(vreg[i][j] >> 16);
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = tid + i * kThreads;
+        const int r = min(c >> 4, S - 1 - k0);
+        const uint16_t* rp = ub + r * rs + 8 * (c & 15);
+        kreg[i] = *reinterpret_cast<const u32x4_t*>(rp + D);
+        vreg[i] = *reinterpret_cast<const u32x4_t*>(rp + 2 * D);
       }
     }
   };
-
-  const int nkt = (S + kBN - 1) / kBN;
-  load_tile(0);
-  store_tile();
-  __syncthreads();
-
-  const int prow0 = perm_row(l32);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * kBN;
-    if (kt + 1 < nkt) load_tile(k0 + kBN);
-
-    // S^T (keys x queries) for two 32-key sub-tiles.
-    f32x16_t acc_s[2];
+  auto store_unit = [&](int stage) {
+    unsigned char* ks = smem + stage * kStage;
 #pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-      acc_s[sg] = f32x16_t{};
-      const unsigned char* kp = ks + (32 * sg + prow0) * kKPitch + 16 * hi;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp + 32 * k);
-        acc_s[sg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], acc_s[sg], 0, 0, 0);
-      }
+    for (int i = 0; i < kChunks; ++i) {
+      *reinterpret_cast<u32x4_t*>(ks + sk_off[i]) = kreg[i];
+      *reinterpret_cast<u32x4_t*>(ks + kKBytes + sv_off[i]) = vreg[i];
     }
+  };
 
-    // Mask keys past the end (only the last tile can have them).
-    if (k0 + kBN > S) {
-#pragma unroll
-      for (int sg = 0; sg < 2; ++sg)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int g = i >> 2, r = i & 3;
-          const int key = k0 + 32 * sg + 16 * (g >> 1) + 8 * hi + 4 * (g & 1) + r;
-          if (key >= S) acc_s[sg][i] = -INFINITY;
-        }
-    }
+  // Per-lane LDS offsets: K A-operand row l16 at channel 8*grp; V^T source row
+  // 4*grp + l16/4 at channel 4*(l16%4).
+  const int k_off = l16 * kKPitch + 16 * grp;
+  const int v_off = kKBytes + (4 * grp + (l16 >> 2)) * kVPitch + 8 * (l16 & 3);
 
-    // Online softmax (base-2, scale folded in).
-    float mx = acc_s[0][0];
+  // S^T of one unit: 2 key tiles (16 keys) x 2 query tiles, over 128 channels.
+  auto scores = [&](int stage, f32x4_t (&acc)[2][2]) {
+    const unsigned char* ks = smem + stage * kStage + k_off;
 #pragma unroll
-    for (int sg = 0; sg < 2; ++sg)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[sg][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8_t pf[4];
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8_t v;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[sg][8 * half + j], scale_log2, -m_new));
-          psum += p;
-          v[j] = (__bf16)p;
-        }
-        pf[2 * sg + half] = v;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[dt][i] *= alpha;
-
-    // O^T (channels x queries) += V^T P^T over the 64 keys of the tile.
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const unsigned char* vp = vs + (32 * dt + l32) * kVPitch + 16 * hi;
+    for (int t = 0; t < 2; ++t) {
+      acc[t][0] = acc[t][1] = f32x4_t{};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vp + 32 * k);
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k], acc_o[dt], 0, 0, 0);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + 16 * t * kKPitch + 64 * k);
+        acc[t][0] = mfma16(a, qf[0][k], acc[t][0]);
+        acc[t][1] = mfma16(a, qf[1][k], acc[t][1]);
+      }
+    }
+  };
+
+  const int nu = (S + kBN - 1) / kBN;
+  load_unit(0);
+  store_unit(0);
+  if (nu > 1) {
+    load_unit(kBN);
+    store_unit(1);
+  }
+  __syncthreads();
+  if (nu > 2) load_unit(2 * kBN);
+  f32x4_t sc[2][2];
+  scores(0, sc);
+
+  for (int un = 0; un < nu; ++un) {
+    const int k0 = un * kBN;
+    // LDS holds units un and un+1 (stages un%4, (un+1)%4); unit un+2 is in registers.
+
+    if (k0 + kBN > S) {  // mask keys past the end (last unit only)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + 16 * t + 4 * grp + i >= S) sc[t][0][i] = sc[t][1][i] = -INFINITY;
+    }
+
+    // Running max per query column (base-2, scale folded in), lazily moved.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float mx = fmaxf(fmaxf(sc[0][u][0], sc[0][u][1]), fmaxf(sc[0][u][2], sc[0][u][3]));
+      mx = fmaxf(mx, fmaxf(fmaxf(sc[1][u][0], sc[1][u][1]), fmaxf(sc[1][u][2], sc[1][u][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+      if (__ballot(mx > m_run[u] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run[u], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
+        m_run[u] = m_new;
+        l_run[u] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
       }
     }
 
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      store_tile();
-      __syncthreads();
+    // Scores of the next unit (MFMA) overlap the exponentials of this one
+    // (VALU). On the last unit the stage read is stale but in bounds and the
+    // result is discarded; computing it unconditionally keeps the MFMAs and
+    // the exponentials in one basic block so they can be interleaved.
+    f32x4_t sn[2][2];
+    scores((un + 1) % kStages, sn);
+
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float psum = 0.f;
+      bf16x8_t v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[j >> 2][u][j & 3], scale_log2, -m_run[u]));
+        psum += p;
+        v[j] = (__bf16)p;
+      }
+      pf[u] = v;
+      l_run[u] += psum;
     }
+#if WAN_ATTN_SCHED
+    // Issue order: the 8 K reads of the next unit, then each of its 16 MFMAs
+    // followed by a share of the exponential / conversion VALU work.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, WAN_ATTN_SCHED, 0);
+    }
+#endif
+
+    // O^T (channels x queries) += V^T P^T: 8 channel tiles, one 32-key step.
+    {
+      const unsigned char* vp = smem + (un % kStages) * kStage + v_off;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const s16x4_t lo = lds_read_tr16(vp + 32 * dt);
+        const s16x4_t hi4 = lds_read_tr16(vp + 16 * kVPitch + 32 * dt);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc_o[dt][0] = mfma16(a, pf[0], acc_o[dt][0]);
+        acc_o[dt][1] = mfma16(a, pf[1], acc_o[dt][1]);
+      }
+    }
+
+    // Stage (un+2)%4 last held unit un-2, which every wave finished in an
+    // earlier iteration (barrier below), so unit un+2 can be written now.
+    store_unit((un + 2) % kStages);  // past the end: stale registers into a stage no longer read
+    __syncthreads();
+    if (un + 3 < nu) load_unit((un + 3) * kBN);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sc[t][0] = sn[t][0], sc[t][1] = sn[t][1];
   }
 
-  // Epilogue: O = O^T / l, bf16; lane holds 4 consecutive channels per (dt, g).
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (qrow < S) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = out + ((int64_t)b * S + qrow) * D + h * kD + 4 * hi;
+  // Epilogue: O = O^T / l in bf16; lane holds 4 consecutive channels per (dt, u).
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int u = 0; u < 2; ++u) {
+    float l_tot = l_run[u] + __shfl_xor(l_run[u], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int q = q0 + 16 * u + l16;
+    if (q < S) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* op = out + ((int64_t)b * S + q) * D + h * kD + 4 * grp;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int dt = 0; dt < 8; ++dt) {
         uint2 w;
-        w.x = pack_bf16x2(acc_o[dt][4 * g + 0] * inv, acc_o[dt][4 * g + 1] * inv);
-        w.y = pack_bf16x2(acc_o[dt][4 * g + 2] * inv, acc_o[dt][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * g) = w;
+        w.x = pack_bf16x2(acc_o[dt][u][0] * inv, acc_o[dt][u][1] * inv);
+        w.y = pack_bf16x2(acc_o[dt][u][2] * inv, acc_o[dt][u][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * dt) = w;
       }
-    if (lse && hi == 0) lse[(int64_t)bh * S + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      if (lse && grp == 0) lse[(int64_t)bh * S + q] = (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f;
+    }
   }
 }
 

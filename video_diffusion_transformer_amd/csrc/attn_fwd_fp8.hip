@@ -1,0 +1,246 @@
+// Bidirectional multi-head attention with fp8 (OCP e4m3) operands and fp32
+// accumulation on the gfx950 v_mfma_scale_f32_16x16x128_f8f6f4 (unit block
+// scales), the fp8 configuration of the Wan2.2 720p step. The TensorRT-LLM pull
+// request "Optimize Wan2.2 Dataflow" runs this attention in FP8 through a cuDNN
+// flash SDPA kernel (Isolated Operator Results); this kernel is written from the
+// definition, not from that one.
+//
+// Inputs come from the quantisation pass: Q and K in a packed [B, S, 2D] e4m3
+// buffer, V transposed per head [B, heads, 128, S_pad] e4m3, and the three
+// per-tensor scales (x8 = x * scale). Scores are q8 . k8 / (scale_q scale_k)
+// * softmax_scale; the softmax is fp32 (base 2, scale folded in); P is
+// quantised to e4m3 at a fixed scale of 2^8 and the output is
+// (sum p8 v8) / (2^8 * scale_v * l), with l the fp32 sum of P.
+//
+// Work decomposition (same skeleton as the bf16 kernel):
+//   * workgroup = 4 waves = 128 queries of one (b, h); each wave owns 32 queries
+//     (two 16-column MFMA tiles);
+//   * keys stream in units of 128 (one K = 128 MFMA step for PV) through two LDS
+//     stages, the next unit prefetched into registers during the MFMAs;
+//   * S^T = K Q^T: one 16x16x128 MFMA covers all 128 channels of a 16-key tile.
+//     The K rows are fed in a permuted order -- tile t, A-row m takes key
+//     32*(m/4) + 4t + m%4 -- so that after the 8 tiles lane group g holds the
+//     scores of keys 32g .. 32g+31 in order, which is exactly the k layout of the
+//     B operand of O^T = V^T P^T: the quantised probabilities need no shuffle;
+//   * K and V^T tiles are 128 x 128 bytes in LDS with an XOR swizzle of the
+//     16-byte chunk (K: by bits 5-6 and 1 of the row, V^T: by bits 1-3) so the
+//     16 rows each 16-lane group reads land in distinct banks;
+//   * the running max moves only when a unit's max exceeds it by more than 0.75
+//     (log2 units): p <= 2^0.75, so p * 2^8 <= 431 stays inside e4m3.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace wan {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBN = 128;                 // keys per unit
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;
+constexpr int kTile = 128 * 128;         // bytes of one K or V^T tile
+constexpr int kStage = 2 * kTile;
+constexpr float kPScale = 256.0f;        // P is quantised as e4m3(p * 2^8)
+constexpr float kRescaleSlack = 0.75f;   // keeps p * 2^8 <= 2^8.75 < 448
+
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  const int xcd = bid & 7, j = bid >> 3;
+  const int q = nb >> 3, r = nb & 7;
+  return xcd * q + (xcd < r ? xcd : r) + j;
+}
+
+// Physical byte offset of logical 16-byte chunk `ch` of row `r` in a K tile / V^T tile.
+__device__ __forceinline__ int k_swz(int r, int ch) { return r * 128 + 16 * (ch ^ (((r >> 5) & 3) | (((r >> 1) & 1) << 2))); }
+__device__ __forceinline__ int v_swz(int r, int ch) { return r * 128 + 16 * (ch ^ ((r >> 1) & 7)); }
+
+__device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c) {
+  // e4m3 x e4m3 (format code 0 for both), block scales 2^(127-127) = 1.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__global__ void __launch_bounds__(kThreads, 2)
+attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__ vt8,
+                    const float* __restrict__ scales, uint16_t* __restrict__ out, float* __restrict__ lse, int S,
+                    int S_pad, int heads, int nqt, float softmax_scale) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
+
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = lid % nqt;
+  const int bh = lid / nqt;
+  const int h = bh % heads, b = bh / heads;
+  const int D = heads * kD;
+  const int rs = 2 * D;  // bytes per token row of qk8
+  const uint8_t* qkb = qk8 + (int64_t)b * S * rs + h * kD;
+  const uint8_t* vtb = vt8 + (int64_t)bh * kD * S_pad;
+
+  const float dq = 1.0f / scales[0], dk = 1.0f / scales[1], dv = 1.0f / scales[2];
+  const float c_log2 = dq * dk * softmax_scale * 1.4426950408889634f;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+
+  // Q fragments: query 16u + l16, channels 32*grp .. +31 (32 bytes).
+  const int q0 = qt * kBM + wave * 32;
+  i32x8_t qf[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    int q = q0 + 16 * u + l16;
+    q = q < S ? q : S - 1;
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(qkb + (int64_t)q * rs + 32 * grp);
+    const u32x4_t x0 = qp[0], x1 = qp[1];
+    qf[u] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+  }
+
+  f32x4_t acc_o[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc_o[i][0] = acc_o[i][1] = f32x4_t{};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  // Staging: K unit = 128 rows x 8 chunks, V^T unit = 128 rows x 8 chunks; c = tid + 256 i.
+  u32x4_t kreg[4], vreg[4];
+  auto load_unit = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c >> 3, ch = c & 7;
+      const int key = min(k0 + r, S - 1);
+      kreg[i] = *reinterpret_cast<const u32x4_t*>(qkb + (int64_t)key * rs + D + 16 * ch);
+      vreg[i] = *reinterpret_cast<const u32x4_t*>(vtb + (int64_t)r * S_pad + k0 + 16 * ch);
+    }
+  };
+  auto store_unit = [&](int stage) {
+    unsigned char* ks = smem + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c >> 3, ch = c & 7;
+      *reinterpret_cast<u32x4_t*>(ks + k_swz(r, ch)) = kreg[i];
+      *reinterpret_cast<u32x4_t*>(ks + kTile + v_swz(r, ch)) = vreg[i];
+    }
+  };
+
+  const int nu = (S + kBN - 1) / kBN;
+  load_unit(0);
+  store_unit(0);
+  __syncthreads();
+
+  for (int un = 0; un < nu; ++un) {
+    const int k0 = un * kBN;
+    const unsigned char* ks = smem + (un & 1) * kStage;
+    const unsigned char* vs = ks + kTile;
+
+    // S^T for 8 key tiles; tile t, A-row l16 holds key 32*(l16/4) + 4t + l16%4.
+    f32x4_t acc_s[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = 32 * (l16 >> 2) + 4 * t + (l16 & 3);
+      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(ks + k_swz(r, 2 * grp));
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(ks + k_swz(r, 2 * grp + 1));
+      const i32x8_t a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      acc_s[t][0] = mfma_fp8(a, qf[0], f32x4_t{});
+      acc_s[t][1] = mfma_fp8(a, qf[1], f32x4_t{});
+    }
+
+    // Prefetch the next unit after the score MFMAs so the staging registers are
+    // not live while all eight score tiles are.
+    if (un + 1 < nu) load_unit(k0 + kBN);
+
+    if (k0 + kBN > S) {  // keys past the end (last unit only): lane group grp holds keys 32grp + 4t + i
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + 32 * grp + 4 * t + i >= S) acc_s[t][0][i] = acc_s[t][1][i] = -INFINITY;
+    }
+
+    i32x8_t pf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float mx = fmaxf(acc_s[0][u][0], acc_s[0][u][1]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = (t == 0 ? 2 : 0); i < 4; i += 2) mx = fmaxf(mx, fmaxf(acc_s[t][u][i], acc_s[t][u][i + 1]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c_log2;
+      if (__ballot(mx > m_run[u] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run[u], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
+        m_run[u] = m_new;
+        l_run[u] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf(acc_s[t][u][i], c_log2, -m_run[u]));
+          psum += p[i];
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * kPScale, p[1] * kPScale, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * kPScale, p[3] * kPScale, w, true);
+        pf[u][t] = w;
+      }
+      l_run[u] += psum;
+    }
+
+    // O^T += V^T P^T: 8 channel tiles, K = the 128 keys of the unit.
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int r = 16 * dt + l16;
+      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(vs + v_swz(r, 2 * grp));
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(vs + v_swz(r, 2 * grp + 1));
+      const i32x8_t a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      acc_o[dt][0] = mfma_fp8(a, pf[0], acc_o[dt][0]);
+      acc_o[dt][1] = mfma_fp8(a, pf[1], acc_o[dt][1]);
+    }
+
+    __syncthreads();  // every wave is done with this stage and with the previous one
+    if (un + 1 < nu) {
+      store_unit((un + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  const float out_scale = dv / kPScale;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float l_tot = l_run[u] + __shfl_xor(l_run[u], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int q = q0 + 16 * u + l16;
+    if (q < S) {
+      const float inv = out_scale / l_tot;
+      uint16_t* op = out + ((int64_t)b * S + q) * D + h * kD + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint2 w;
+        w.x = pack_bf16x2(acc_o[dt][u][0] * inv, acc_o[dt][u][1] * inv);
+        w.y = pack_bf16x2(acc_o[dt][u][2] * inv, acc_o[dt][u][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+      }
+      if (lse && grp == 0) lse[(int64_t)bh * S + q] = (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_fp8(const void* qk8, const void* vt8, const float* scales, void* out, float* lse, int B,
+                               int S, int heads, float softmax_scale, hipStream_t stream) {
+  const int nqt = (S + kBM - 1) / kBM;
+  const int64_t nblocks = (int64_t)nqt * heads * B;
+  if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const int S_pad = (S + 127) / 128 * 128;
+  hipLaunchKernelGGL(attn_fwd_fp8_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(qk8), static_cast<const uint8_t*>(vt8), scales,
+                     static_cast<uint16_t*>(out), lse, S, S_pad, heads, nqt, softmax_scale);
+  return hipGetLastError();
+}
+
+}  // namespace wan

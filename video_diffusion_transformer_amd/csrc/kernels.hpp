@@ -17,4 +17,13 @@ hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const f
 hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S, int heads,
                            float softmax_scale, hipStream_t stream);
 
+// fp8: per-tensor amax + e4m3 quantisation into qk8 [B, S, 2D] and
+// vt8 [B, heads, 128, S_pad] (V transposed per head, zero past S).
+hipError_t launch_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int B, int S,
+                                int heads, hipStream_t stream);
+
+// fp8 attention forward from the quantised buffers.
+hipError_t launch_attn_fwd_fp8(const void* qk8, const void* vt8, const float* scales, void* out, float* lse, int B,
+                               int S, int heads, float softmax_scale, hipStream_t stream);
+
 }  // namespace wan

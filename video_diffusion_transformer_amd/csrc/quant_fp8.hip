@@ -1,0 +1,145 @@
+// Per-tensor fp8 (OCP e4m3) quantisation of Q, K and V for the fp8 attention
+// path: amax of each tensor over all (B, S, D), scale = 448 / amax (fp32, IEEE
+// division; an all-zero tensor keeps scale 1), e4m3 = round-to-nearest-even of
+// fl32(x * scale), saturated to +-448. This is the amax -> E4M3 scale -> quantise
+// recipe the TensorRT-LLM pull request "Optimize Wan2.2 Dataflow" fuses for its
+// FFN activation (change 2), applied here to the attention inputs.
+//
+// Layout of the outputs (our own, consumed only by the fp8 attention kernel):
+//   qk8 : [B, S, 2D] bytes -- per token Q (all heads) then K (all heads);
+//   vt8 : [B, heads, 128, S_pad] bytes -- V transposed per head (channel-major,
+//         keys contiguous), S_pad = S rounded up to 128, zero past S. Writing V
+//         transposed costs no extra traffic (V is written once either way) and
+//         lets the attention kernel read the PV operand with plain 16-byte LDS
+//         loads.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace wan {
+
+namespace {
+
+constexpr int kTok = 64;  // tokens per quantisation tile
+
+__global__ void amax_clear_kernel(float* amax) {
+  if (threadIdx.x < 3) amax[threadIdx.x] = 0.f;
+}
+
+// Grid-stride over token rows; each block folds |x| of Q, K and V separately and
+// publishes three atomic maxima (non-negative floats order like their bits).
+__global__ void __launch_bounds__(256) amax_kernel(const uint16_t* __restrict__ qkv, float* amax, int64_t rows,
+                                                   int D) {
+  const int chunks = 3 * D / 8, per = D / 8;
+  float m[3] = {0.f, 0.f, 0.f};
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* row = qkv + r * 3 * (int64_t)D;
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + 8 * c);
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(v[j])), fabsf(bf16_hi(v[j]))));
+      const int part = c / per;
+      m[0] = part == 0 ? fmaxf(m[0], a) : m[0];
+      m[1] = part == 1 ? fmaxf(m[1], a) : m[1];
+      m[2] = part == 2 ? fmaxf(m[2], a) : m[2];
+    }
+  }
+  __shared__ float red[4][3];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    float x = m[p];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    if (lane == 0) red[wave][p] = x;
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    float x = red[0][threadIdx.x];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) x = fmaxf(x, red[w][threadIdx.x]);
+    atomicMax(reinterpret_cast<unsigned int*>(amax) + threadIdx.x, __float_as_uint(x));
+  }
+}
+
+__device__ __forceinline__ float scale_of(float amax) { return amax > 0.f ? 448.0f / amax : 1.0f; }
+
+// Eight bf16 (one 16-byte chunk) -> eight e4m3 bytes.
+__device__ __forceinline__ uint2 quant8(const u32x4_t v, float s) {
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float x0 = fminf(fmaxf(bf16_lo(v[2 * h]) * s, -448.f), 448.f);
+    const float x1 = fminf(fmaxf(bf16_hi(v[2 * h]) * s, -448.f), 448.f);
+    const float x2 = fminf(fmaxf(bf16_lo(v[2 * h + 1]) * s, -448.f), 448.f);
+    const float x3 = fminf(fmaxf(bf16_hi(v[2 * h + 1]) * s, -448.f), 448.f);
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, p, true);
+    w[h] = static_cast<uint32_t>(p);
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// One block = 64 tokens of one (b, head): Q and K rows are quantised in place
+// of their packed position; V goes through LDS to be stored channel-major.
+__global__ void __launch_bounds__(256)
+quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_t* __restrict__ vt8,
+             const float* __restrict__ amax, float* __restrict__ scales, int S, int S_pad, int heads) {
+  __shared__ uint8_t vt[128][kTok + 16];
+  const int h = blockIdx.y, b = blockIdx.z, s0 = blockIdx.x * kTok;
+  const int D = heads * 128;
+  const float sq = scale_of(amax[0]), sk = scale_of(amax[1]), sv = scale_of(amax[2]);
+  if (blockIdx.x == 0 && h == 0 && b == 0 && threadIdx.x == 0) {
+    scales[0] = sq;
+    scales[1] = sk;
+    scales[2] = sv;
+  }
+  // 64 tokens x 16 chunks of 8 channels = 1024 chunks, 4 per thread.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int t = c >> 4, ch = c & 15;
+    const int s = s0 + t;
+    uint2 vq = make_uint2(0, 0);
+    if (s < S) {
+      const uint16_t* row = qkv + ((int64_t)b * S + s) * 3 * (int64_t)D + h * 128 + 8 * ch;
+      uint8_t* orow = qk8 + ((int64_t)b * S + s) * 2 * (int64_t)D + h * 128 + 8 * ch;
+      *reinterpret_cast<uint2*>(orow) = quant8(*reinterpret_cast<const u32x4_t*>(row), sq);
+      *reinterpret_cast<uint2*>(orow + D) = quant8(*reinterpret_cast<const u32x4_t*>(row + D), sk);
+      vq = quant8(*reinterpret_cast<const u32x4_t*>(row + 2 * D), sv);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vt[8 * ch + j][t] = static_cast<uint8_t>(vq.x >> (8 * j));
+      vt[8 * ch + 4 + j][t] = static_cast<uint8_t>(vq.y >> (8 * j));
+    }
+  }
+  __syncthreads();
+  // 128 channel rows x 64 keys = 128 x 4 chunks of 16 B, 2 per thread.
+  uint8_t* vbase = vt8 + (((int64_t)b * heads + h) * 128) * S_pad + s0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int d = c >> 2, part = c & 3;
+    *reinterpret_cast<u32x4_t*>(vbase + (int64_t)d * S_pad + 16 * part) =
+        *reinterpret_cast<const u32x4_t*>(&vt[d][16 * part]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int B, int S,
+                                int heads, hipStream_t stream) {
+  const int D = heads * 128;
+  const int64_t rows = (int64_t)B * S;
+  const int S_pad = (S + 127) / 128 * 128;
+  hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(64), 0, stream, amax);
+  const int64_t nb = rows < 8192 ? rows : 8192;
+  hipLaunchKernelGGL(amax_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qkv), amax, rows, D);
+  hipLaunchKernelGGL(quant_kernel, dim3(S_pad / kTok, heads, B), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qkv), static_cast<uint8_t*>(qk8), static_cast<uint8_t*>(vt8),
+                     amax, scales, S, S_pad, heads);
+  return hipGetLastError();
+}
+
+}  // namespace wan

@@ -103,4 +103,60 @@ inline int validate_attn(const void* qkv, const void* out, const void* lse, int6
   return WAN_OK;
 }
 
+// Bytes of the transposed fp8 V buffer: B * heads * 128 * S_pad, S_pad = S rounded up to 128.
+inline bool fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t* out) {
+  const int64_t s_pad = (S + 127) / 128 * 128;
+  int64_t t;
+  return mul_ok(B, heads, &t) && mul_ok(t, kHeadDim, &t) && mul_ok(t, s_pad, out);
+}
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+inline int validate_quant_fp8(const void* qkv, const void* qk8, const void* vt8, const void* scales,
+                              const void* amax, int64_t B, int64_t S, int64_t heads, int64_t head_dim,
+                              Sizes* z) {
+  int rc = check_sizes(B, S, heads, head_dim, z);
+  if (rc != WAN_OK) return rc;
+  if (B > kMaxGridYZ) return WAN_E_OVERFLOW;
+  if (z->empty) return WAN_OK;
+  if (!qkv || !qk8 || !vt8 || !scales || !amax) return WAN_E_NULL;
+  if (!aligned(qkv, 16) || !aligned(qk8, 16) || !aligned(vt8, 16) || !aligned(scales, 4) || !aligned(amax, 4))
+    return WAN_E_ALIGN;
+  int64_t vt_bytes;
+  if (!fp8_vt_bytes(B, S, heads, &vt_bytes)) return WAN_E_OVERFLOW;
+  const int64_t in_bytes = z->qkv_elems * 2, qk_bytes = z->rows * 2 * z->D;
+  const void* outs[4] = {qk8, vt8, scales, amax};
+  const int64_t sizes[4] = {qk_bytes, vt_bytes, 12, 12};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(outs[i], sizes[i], qkv, in_bytes)) return WAN_E_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], sizes[i], outs[j], sizes[j])) return WAN_E_ALIAS;
+  }
+  return WAN_OK;
+}
+
+inline int validate_attn_fp8(const void* qk8, const void* vt8, const void* scales, const void* out,
+                             const void* lse, int64_t B, int64_t S, int64_t heads, int64_t head_dim, float scale,
+                             Sizes* z) {
+  int rc = check_sizes(B, S, heads, head_dim, z);
+  if (rc != WAN_OK) return rc;
+  if (!std::isfinite(scale) || scale <= 0.f) return WAN_E_VALUE;
+  if (z->empty) return WAN_OK;
+  if (!qk8 || !vt8 || !scales || !out) return WAN_E_NULL;
+  if (!aligned(qk8, 16) || !aligned(vt8, 16) || !aligned(scales, 4) || !aligned(out, 16) ||
+      (lse && !aligned(lse, 4)))
+    return WAN_E_ALIGN;
+  int64_t vt_bytes;
+  if (!fp8_vt_bytes(B, S, heads, &vt_bytes)) return WAN_E_OVERFLOW;
+  const int64_t qk_bytes = z->rows * 2 * z->D, out_bytes = z->out_elems * 2, lse_bytes = z->B * z->heads * z->S * 4;
+  const void* ins[3] = {qk8, vt8, scales};
+  const int64_t in_sizes[3] = {qk_bytes, vt_bytes, 12};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(out, out_bytes, ins[i], in_sizes[i])) return WAN_E_ALIAS;
+    if (lse && overlaps(lse, lse_bytes, ins[i], in_sizes[i])) return WAN_E_ALIAS;
+  }
+  if (lse && overlaps(lse, lse_bytes, out, out_bytes)) return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 }  // namespace wan

@@ -6,7 +6,8 @@ live on the GPU; there is no CPU path. If the library is not built the first
 call raises -- nothing falls back to another implementation.
 
 The names follow the C ABI: ``qknorm_rope`` -> wan_qknorm_rope,
-``attn_fwd`` -> wan_attn_fwd.
+``attn_fwd`` -> wan_attn_fwd, ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
+``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
 """
 
 import ctypes
@@ -34,6 +35,9 @@ SIGNATURES = {
     "wan_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
+    "wan_qkv_quant_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "wan_fp8_vt_bytes": (ctypes.c_int64, [_I64, _I64, _I64, _I64]),
+    "wan_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
 }
 
 
@@ -144,4 +148,71 @@ def attn_fwd(qkv, heads, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=Fa
         _check("wan_attn_fwd", lib().wan_attn_fwd(
             _ptr(qkv), _ptr(out), _ptr(lse) if want_lse else ctypes.c_void_p(0), B, S, heads,
             head_dim, scale, _stream(qkv.device, stream)))
+    return (out, lse) if want_lse else out
+
+
+class Fp8QKV:
+    """Outputs of qkv_quant_fp8: qk8 [B, S, 2D] and vt8 [B, heads, 128, S_pad]
+    e4m3 bytes (uint8 tensors), per-tensor scales and amax (fp32 [3])."""
+
+    def __init__(self, qk8, vt8, scales, amax, B, S, heads):
+        self.qk8, self.vt8, self.scales, self.amax = qk8, vt8, scales, amax
+        self.B, self.S, self.heads = B, S, heads
+
+    @property
+    def s_pad(self):
+        return (self.S + 127) // 128 * 128
+
+
+def fp8_buffers(B, S, heads, device, head_dim=HEAD_DIM):
+    """Allocate the buffers qkv_quant_fp8 writes."""
+    D = heads * head_dim
+    n = lib().wan_fp8_vt_bytes(B, S, heads, head_dim)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return Fp8QKV(torch.empty((B, S, 2 * D), dtype=torch.uint8, device=device),
+                  torch.empty(n, dtype=torch.uint8, device=device),
+                  torch.empty(3, dtype=torch.float32, device=device),
+                  torch.empty(3, dtype=torch.float32, device=device), B, S, heads)
+
+
+def qkv_quant_fp8(qkv, heads, head_dim=HEAD_DIM, out=None, stream=None):
+    """Per-tensor e4m3 quantisation of the packed bf16 [B, S, 3D] buffer.
+    Returns an Fp8QKV (allocated unless ``out`` is given)."""
+    _need_gpu("qkv", qkv, torch.bfloat16)
+    B, S = qkv.shape[0], qkv.shape[1]
+    if qkv.dim() != 3 or qkv.shape[2] != 3 * heads * head_dim:
+        raise ValueError("qkv must be [B, S, 3*heads*head_dim]")
+    f = out if out is not None else fp8_buffers(B, S, heads, qkv.device, head_dim)
+    for name in ("qk8", "vt8"):
+        _need_gpu(name, getattr(f, name), torch.uint8)
+    _need_gpu("scales", f.scales, torch.float32)
+    _need_gpu("amax", f.amax, torch.float32)
+    if f.vt8.numel() < lib().wan_fp8_vt_bytes(B, S, heads, head_dim) or f.qk8.numel() != B * S * 2 * heads * head_dim:
+        raise ValueError("fp8 buffers are too small for these sizes")
+    with torch.cuda.device(qkv.device):
+        _check("wan_qkv_quant_fp8", lib().wan_qkv_quant_fp8(
+            _ptr(qkv), _ptr(f.qk8), _ptr(f.vt8), _ptr(f.scales), _ptr(f.amax), B, S, heads, head_dim,
+            _stream(qkv.device, stream)))
+    return f
+
+
+def attn_fwd_fp8(f, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=False, stream=None):
+    """Attention from an Fp8QKV. Returns out [B, S, D] bf16 (and lse)."""
+    B, S, heads = f.B, f.S, f.heads
+    D = heads * head_dim
+    scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else float(softmax_scale)
+    dev = f.qk8.device
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=dev)
+    _need_gpu("out", out, torch.bfloat16)
+    want_lse = lse is not False and lse is not None
+    if lse is True:
+        lse = torch.empty((B, heads, S), dtype=torch.float32, device=dev)
+    if want_lse:
+        _need_gpu("lse", lse, torch.float32)
+    with torch.cuda.device(dev):
+        _check("wan_attn_fwd_fp8", lib().wan_attn_fwd_fp8(
+            _ptr(f.qk8), _ptr(f.vt8), _ptr(f.scales), _ptr(out), _ptr(lse) if want_lse else ctypes.c_void_p(0),
+            B, S, heads, head_dim, scale, _stream(dev, stream)))
     return (out, lse) if want_lse else out
