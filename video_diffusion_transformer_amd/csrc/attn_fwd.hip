@@ -9,11 +9,10 @@
 // Work decomposition
 //   * one workgroup = 4 wavefronts = 128 query rows of one (b, h); each wave owns
 //     32 rows (two 16-row MFMA column tiles) for the whole kernel;
-//   * keys stream in units of 32 through a ring of four LDS stages. In the
-//     iteration that consumes unit j, the scores of unit j+1 are computed (MFMA)
-//     while the exponentials of unit j run (VALU), then PV of unit j; unit j+2,
-//     loaded into registers one iteration earlier, is written to the stage unit
-//     j-2 used, and one barrier per unit publishes it;
+//   * keys stream in tiles of 64 through two LDS stages, filled straight from
+//     global memory by global_load_lds_dwordx4 (no staging registers): tile j+1
+//     is requested at the top of the iteration that consumes tile j, and one
+//     wait + barrier per tile publishes it;
 //   * scores are computed transposed, S^T = K Q^T (16x16x32 MFMA: A = 16 keys x
 //     32 channels from LDS, B = Q held in registers), so after the MFMA each
 //     lane holds scores of ONE query column: the online-softmax max and sum are
@@ -25,6 +24,10 @@
 //     lane i receives element i%4 of the 8 bytes lane 4j+i/4 addressed, so 16
 //     lanes addressing 4 key rows x 16 channels each receive one channel with
 //     its 4 keys), pointed at exactly those key rows;
+//   * K and V rows (256 B) are stored unpadded with an XOR swizzle of the 16-byte
+//     chunk index (K: chunk ^ (row % 16), V: chunk ^ 2*(row % 8)), so the 16 K
+//     rows one lane group reads, and the 8 V rows x 32 B half a wave reads with
+//     the transposing load, fall in distinct banks;
 //   * the O^T accumulator keeps one query column per lane, so the rescale by
 //     exp2(m_old - m_new) is lane-local. The running max only moves when a
 //     tile's max exceeds it by more than 8 (log2 units): most tiles skip the
@@ -42,30 +45,25 @@ namespace wan {
 namespace {
 
 constexpr int kD = 128;                  // head dim
-constexpr int kBN = 32;                  // keys per pipeline unit
-constexpr int kStages = 4;               // LDS ring of K/V units
+constexpr int kBN = 64;                  // keys per tile
 constexpr int kWaves = 4;                // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;         // query rows per workgroup
-#ifndef WAN_ATTN_KPAD
-#define WAN_ATTN_KPAD 16
-#endif
-#ifndef WAN_ATTN_VPAD
-#define WAN_ATTN_VPAD 32
-#endif
-constexpr int kKPitch = kD * 2 + WAN_ATTN_KPAD;  // K row pitch in LDS: 16 rows at distinct 4-bank offsets (b128 reads)
-constexpr int kVPitch = kD * 2 + WAN_ATTN_VPAD;  // V row pitch: 8 rows x 32 B tile the 64 banks (transposed b64 reads)
-constexpr int kKBytes = kBN * kKPitch;
-constexpr int kVBytes = kBN * kVPitch;
-constexpr int kStage = kKBytes + kVBytes;
-constexpr int kChunks = kBN * 16 / kThreads;  // 16-byte chunks of K (and of V) per thread per unit
+constexpr int kRow = kD * 2;             // bytes per K or V row
+constexpr int kTile = kBN * kRow;        // 16 KB
+constexpr int kStage = 2 * kTile;        // K tile + V tile
 constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag behind the true max
+constexpr int kWaitVmem0 = 0x0f70;       // s_waitcnt vmcnt(0), other counters unconstrained
 
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   const int xcd = bid & 7, j = bid >> 3;
   const int q = nb >> 3, r = nb & 7;
   return xcd * q + (xcd < r ? xcd : r) + j;
 }
+
+// Logical 16-byte chunk ch of row r sits at physical chunk ch ^ xor(r).
+__device__ __forceinline__ int k_xor(int r) { return r & 15; }
+__device__ __forceinline__ int v_xor(int r) { return 2 * (r & 7); }
 
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -74,7 +72,7 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, float* __restrict__ lse,
                 int S, int heads, int nqt, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = lid % nqt;
@@ -105,94 +103,70 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
   for (int i = 0; i < 8; ++i) acc_o[i][0] = acc_o[i][1] = f32x4_t{};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  // Staging of one unit (32 keys) of K and V: chunk c = tid + 256 i -> key c/16,
-  // channels 8*(c%16). Offsets are 32-bit element offsets from the unit's first row.
-  int g_off[kChunks], sk_off[kChunks], sv_off[kChunks];
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int c = tid + i * kThreads;
-    g_off[i] = (c >> 4) * rs + 8 * (c & 15);
-    sk_off[i] = (c >> 4) * kKPitch + (c & 15) * 16;
-    sv_off[i] = (c >> 4) * kVPitch + (c & 15) * 16;
-  }
-  u32x4_t kreg[kChunks], vreg[kChunks];
-  auto load_unit = [&](int k0) {
-    const uint16_t* ub = base + (int64_t)k0 * rs;
-    if (k0 + kBN <= S) {
-#pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        kreg[i] = *reinterpret_cast<const u32x4_t*>(ub + g_off[i] + D);
-        vreg[i] = *reinterpret_cast<const u32x4_t*>(ub + g_off[i] + 2 * D);
-      }
-    } else {  // ragged last unit: rows past the end re-read row S-1 (masked later)
-#pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        const int c = tid + i * kThreads;
-        const int r = min(c >> 4, S - 1 - k0);
-        const uint16_t* rp = ub + r * rs + 8 * (c & 15);
-        kreg[i] = *reinterpret_cast<const u32x4_t*>(rp + D);
-        vreg[i] = *reinterpret_cast<const u32x4_t*>(rp + 2 * D);
-      }
-    }
-  };
-  auto store_unit = [&](int stage) {
+  // Direct global -> LDS staging: lane l of a wave instruction lands at the
+  // wave-uniform LDS base + 16*l. Each wave fills four 1 KB blocks (4 rows) of
+  // the K tile and of the V tile; lane l of a block takes physical row
+  // 4*blk + l/16, physical chunk l%16, and fetches the logical chunk the
+  // swizzle maps there. Rows past the end re-read row S-1 (masked later).
+  auto issue_tile = [&](int k0, int stage) {
     unsigned char* ks = smem + stage * kStage;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      *reinterpret_cast<u32x4_t*>(ks + sk_off[i]) = kreg[i];
-      *reinterpret_cast<u32x4_t*>(ks + kKBytes + sv_off[i]) = vreg[i];
+    for (int j = 0; j < 4; ++j) {
+      const int blk = 4 * wave + j;
+      const int r = 4 * blk + (lane >> 4), pc = lane & 15;
+      const uint16_t* rp = base + (int64_t)min(k0 + r, S - 1) * rs;
+      __builtin_amdgcn_global_load_lds(rp + D + 8 * (pc ^ k_xor(r)), ks + blk * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(rp + 2 * D + 8 * (pc ^ v_xor(r)), ks + kTile + blk * 1024, 16, 0, 0);
     }
   };
 
-  // Per-lane LDS offsets: K A-operand row l16 at channel 8*grp; V^T source row
-  // 4*grp + l16/4 at channel 4*(l16%4).
-  const int k_off = l16 * kKPitch + 16 * grp;
-  const int v_off = kKBytes + (4 * grp + (l16 >> 2)) * kVPitch + 8 * (l16 & 3);
+  // Per-lane LDS offsets: K A-operand row l16 (+16t), logical chunk 4k + grp;
+  // V^T source row 4*grp + l16/4 (+32c, +16), channels 32dt + 4*(l16%4).
+  const int vr = 4 * grp + (l16 >> 2);
 
-  // S^T of one unit: 2 key tiles (16 keys) x 2 query tiles, over 128 channels.
-  auto scores = [&](int stage, f32x4_t (&acc)[2][2]) {
-    const unsigned char* ks = smem + stage * kStage + k_off;
+  const int nkt = (S + kBN - 1) / kBN;
+  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * kBN;
+    const unsigned char* ks = smem + (kt & 1) * kStage;
+    const unsigned char* vs = ks + kTile;
+    // The other stage was last read in iteration kt-1, which every wave has left.
+    if (kt + 1 < nkt) issue_tile(k0 + kBN, (kt + 1) & 1);
+
+    // S^T: 4 key tiles (16 keys) x 2 query tiles, K over the 128 channels.
+    f32x4_t acc_s[4][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t][0] = acc[t][1] = f32x4_t{};
+    for (int t = 0; t < 4; ++t) {
+      acc_s[t][0] = acc_s[t][1] = f32x4_t{};
+      const int r = 16 * t + l16;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + 16 * t * kKPitch + 64 * k);
-        acc[t][0] = mfma16(a, qf[0][k], acc[t][0]);
-        acc[t][1] = mfma16(a, qf[1][k], acc[t][1]);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + r * kRow + 16 * ((4 * k + grp) ^ k_xor(r)));
+        acc_s[t][0] = mfma16(a, qf[0][k], acc_s[t][0]);
+        acc_s[t][1] = mfma16(a, qf[1][k], acc_s[t][1]);
       }
     }
-  };
 
-  const int nu = (S + kBN - 1) / kBN;
-  load_unit(0);
-  store_unit(0);
-  if (nu > 1) {
-    load_unit(kBN);
-    store_unit(1);
-  }
-  __syncthreads();
-  if (nu > 2) load_unit(2 * kBN);
-  f32x4_t sc[2][2];
-  scores(0, sc);
-
-  for (int un = 0; un < nu; ++un) {
-    const int k0 = un * kBN;
-    // LDS holds units un and un+1 (stages un%4, (un+1)%4); unit un+2 is in registers.
-
-    if (k0 + kBN > S) {  // mask keys past the end (last unit only)
+    // Mask keys past the end (only the last tile can have them).
+    if (k0 + kBN > S) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (k0 + 16 * t + 4 * grp + i >= S) sc[t][0][i] = sc[t][1][i] = -INFINITY;
+          if (k0 + 16 * t + 4 * grp + i >= S) acc_s[t][0][i] = acc_s[t][1][i] = -INFINITY;
     }
 
-    // Running max per query column (base-2, scale folded in), lazily moved.
+    // Online softmax per query column (base-2, scale folded in), lazily rescaled.
+    bf16x8_t pf[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      float mx = fmaxf(fmaxf(sc[0][u][0], sc[0][u][1]), fmaxf(sc[0][u][2], sc[0][u][3]));
-      mx = fmaxf(mx, fmaxf(fmaxf(sc[1][u][0], sc[1][u][1]), fmaxf(sc[1][u][2], sc[1][u][3])));
+      float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
+#pragma unroll
+      for (int t = 1; t < 4; ++t)
+        mx = fmaxf(mx, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
       if (__ballot(mx > m_run[u] + kRescaleSlack)) {
@@ -205,61 +179,38 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
       }
-    }
-
-    // Scores of the next unit (MFMA) overlap the exponentials of this one
-    // (VALU). On the last unit the stage read is stale but in bounds and the
-    // result is discarded; computing it unconditionally keeps the MFMAs and
-    // the exponentials in one basic block so they can be interleaved.
-    f32x4_t sn[2][2];
-    scores((un + 1) % kStages, sn);
-
-    bf16x8_t pf[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
       float psum = 0.f;
-      bf16x8_t v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[j >> 2][u][j & 3], scale_log2, -m_run[u]));
-        psum += p;
-        v[j] = (__bf16)p;
+      for (int c = 0; c < 2; ++c) {
+        bf16x8_t v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], scale_log2, -m_run[u]));
+          psum += p;
+          v[j] = (__bf16)p;
+        }
+        pf[u][c] = v;
       }
-      pf[u] = v;
       l_run[u] += psum;
     }
-#if WAN_ATTN_SCHED
-    // Issue order: the 8 K reads of the next unit, then each of its 16 MFMAs
-    // followed by a share of the exponential / conversion VALU work.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, WAN_ATTN_SCHED, 0);
-    }
-#endif
 
-    // O^T (channels x queries) += V^T P^T: 8 channel tiles, one 32-key step.
-    {
-      const unsigned char* vp = smem + (un % kStages) * kStage + v_off;
+    // O^T (channels x queries) += V^T P^T: 8 channel tiles x 2 key steps of 32.
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const s16x4_t lo = lds_read_tr16(vp + 32 * dt);
-        const s16x4_t hi4 = lds_read_tr16(vp + 16 * kVPitch + 32 * dt);
+    for (int dt = 0; dt < 8; ++dt) {
+      const int ch = 2 * dt + ((l16 & 3) >> 1), sub = 8 * (l16 & 1);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int r0 = 32 * c + vr, r1 = r0 + 16;
+        const s16x4_t lo = lds_read_tr16(vs + r0 * kRow + 16 * (ch ^ v_xor(r0)) + sub);
+        const s16x4_t hi4 = lds_read_tr16(vs + r1 * kRow + 16 * (ch ^ v_xor(r1)) + sub);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[dt][0] = mfma16(a, pf[0], acc_o[dt][0]);
-        acc_o[dt][1] = mfma16(a, pf[1], acc_o[dt][1]);
+        acc_o[dt][0] = mfma16(a, pf[0][c], acc_o[dt][0]);
+        acc_o[dt][1] = mfma16(a, pf[1][c], acc_o[dt][1]);
       }
     }
 
-    // Stage (un+2)%4 last held unit un-2, which every wave finished in an
-    // earlier iteration (barrier below), so unit un+2 can be written now.
-    store_unit((un + 2) % kStages);  // past the end: stale registers into a stage no longer read
-    __syncthreads();
-    if (un + 3 < nu) load_unit((un + 3) * kBN);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) sc[t][0] = sn[t][0], sc[t][1] = sn[t][1];
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
+    __syncthreads();                          // ... and every wave's; stage kt&1 is free again
   }
 
   // Epilogue: O = O^T / l in bf16; lane holds 4 consecutive channels per (dt, u).

@@ -50,9 +50,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd * q + (xcd < r ? xcd : r) + j;
 }
 
-// Physical byte offset of logical 16-byte chunk `ch` of row `r` in a K tile / V^T tile.
-__device__ __forceinline__ int k_swz(int r, int ch) { return r * 128 + 16 * (ch ^ (((r >> 5) & 3) | (((r >> 1) & 1) << 2))); }
-__device__ __forceinline__ int v_swz(int r, int ch) { return r * 128 + 16 * (ch ^ ((r >> 1) & 7)); }
+// Chunk swizzles: logical 16-byte chunk ch of row r sits at physical chunk ch ^ xor(r).
+__device__ __forceinline__ int k_xor(int r) { return ((r >> 5) & 3) | (((r >> 1) & 1) << 2); }
+__device__ __forceinline__ int v_xor(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int k_swz(int r, int ch) { return r * 128 + 16 * (ch ^ k_xor(r)); }
+__device__ __forceinline__ int v_swz(int r, int ch) { return r * 128 + 16 * (ch ^ v_xor(r)); }
+
+// s_waitcnt with vmcnt = 0 and the other counters at their maximum (no wait).
+constexpr int kWaitVmem0 = 0x0f70;
 
 __device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c) {
   // e4m3 x e4m3 (format code 0 for both), block scales 2^(127-127) = 1.
@@ -97,38 +102,35 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
   for (int i = 0; i < 8; ++i) acc_o[i][0] = acc_o[i][1] = f32x4_t{};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  // Staging: K unit = 128 rows x 8 chunks, V^T unit = 128 rows x 8 chunks; c = tid + 256 i.
-  u32x4_t kreg[4], vreg[4];
-  auto load_unit = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 3, ch = c & 7;
-      const int key = min(k0 + r, S - 1);
-      kreg[i] = *reinterpret_cast<const u32x4_t*>(qkb + (int64_t)key * rs + D + 16 * ch);
-      vreg[i] = *reinterpret_cast<const u32x4_t*>(vtb + (int64_t)r * S_pad + k0 + 16 * ch);
-    }
-  };
-  auto store_unit = [&](int stage) {
+  // Direct global -> LDS staging (global_load_lds_dwordx4: lane l of a wave
+  // instruction lands at the wave-uniform LDS base + 16*l). Each wave fills four
+  // 1 KB blocks (8 rows) of the K tile and of the V^T tile; lane l of a block
+  // takes physical row 8*blk + l/8, physical chunk l%8, so it fetches the
+  // logical chunk that the swizzle maps there.
+  auto issue_unit = [&](int k0, int stage) {
     unsigned char* ks = smem + stage * kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4_t*>(ks + k_swz(r, ch)) = kreg[i];
-      *reinterpret_cast<u32x4_t*>(ks + kTile + v_swz(r, ch)) = vreg[i];
+    for (int j = 0; j < 4; ++j) {
+      const int blk = 4 * wave + j;
+      const int r = 8 * blk + (lane >> 3), pc = lane & 7;
+      const int key = min(k0 + r, S - 1);
+      __builtin_amdgcn_global_load_lds(qkb + (int64_t)key * rs + D + 16 * (pc ^ k_xor(r)), ks + blk * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vtb + (int64_t)r * S_pad + k0 + 16 * (pc ^ v_xor(r)), ks + kTile + blk * 1024,
+                                       16, 0, 0);
     }
   };
 
   const int nu = (S + kBN - 1) / kBN;
-  load_unit(0);
-  store_unit(0);
+  issue_unit(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
 
   for (int un = 0; un < nu; ++un) {
     const int k0 = un * kBN;
     const unsigned char* ks = smem + (un & 1) * kStage;
     const unsigned char* vs = ks + kTile;
+    // The other stage was last read in iteration un-1, which every wave has left.
+    if (un + 1 < nu) issue_unit(k0 + kBN, (un + 1) & 1);
 
     // S^T for 8 key tiles; tile t, A-row l16 holds key 32*(l16/4) + 4t + l16%4.
     f32x4_t acc_s[8][2];
@@ -141,10 +143,6 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
       acc_s[t][0] = mfma_fp8(a, qf[0], f32x4_t{});
       acc_s[t][1] = mfma_fp8(a, qf[1], f32x4_t{});
     }
-
-    // Prefetch the next unit after the score MFMAs so the staging registers are
-    // not live while all eight score tiles are.
-    if (un + 1 < nu) load_unit(k0 + kBN);
 
     if (k0 + kBN > S) {  // keys past the end (last unit only): lane group grp holds keys 32grp + 4t + i
 #pragma unroll
@@ -201,11 +199,8 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
       acc_o[dt][1] = mfma_fp8(a, pf[1], acc_o[dt][1]);
     }
 
-    __syncthreads();  // every wave is done with this stage and with the previous one
-    if (un + 1 < nu) {
-      store_unit((un + 1) & 1);
-      __syncthreads();
-    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of the next unit has landed
+    __syncthreads();                          // ... and every other wave's; this stage is free
   }
 
   const float out_scale = dv / kPScale;
