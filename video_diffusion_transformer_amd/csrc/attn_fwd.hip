@@ -7,8 +7,12 @@
 // denoiser is bidirectional). The S x S score matrix never leaves registers.
 //
 // Work decomposition
-//   * one workgroup = 4 wavefronts = 128 query rows of one (b, h); each wave owns
-//     32 rows (two 16-row MFMA column tiles) for the whole kernel;
+//   * one workgroup = 8 wavefronts = 384 query rows of one (b, h), one
+//     workgroup per CU (two waves per SIMD); each wave owns 48 rows (three
+//     16-row MFMA column tiles) for the whole kernel, so every K/V fragment read
+//     from LDS feeds three MFMAs (LDS bandwidth, not the MFMA rate, is the
+//     tighter limit of this loop on gfx950), and each K/V tile staged in LDS
+//     serves 384 queries;
 //   * keys stream in tiles of 64 through two LDS stages, filled straight from
 //     global memory by global_load_lds_dwordx4 (no staging registers): tile j+1
 //     is requested at the top of the iteration that consumes tile j, and one
@@ -46,9 +50,16 @@ namespace {
 
 constexpr int kD = 128;                  // head dim
 constexpr int kBN = 64;                  // keys per tile
-constexpr int kWaves = 4;                // waves per workgroup
+#ifndef WAN_ATTN_QT
+#define WAN_ATTN_QT 3
+#endif
+#ifndef WAN_ATTN_WAVES
+#define WAN_ATTN_WAVES 8
+#endif
+constexpr int kQT = WAN_ATTN_QT;         // 16-query MFMA column tiles per wave
+constexpr int kWaves = WAN_ATTN_WAVES;   // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;         // query rows per workgroup
+constexpr int kBM = 16 * kQT * kWaves;   // query rows per workgroup
 constexpr int kRow = kD * 2;             // bytes per K or V row
 constexpr int kTile = kBN * kRow;        // 16 KB
 constexpr int kStage = 2 * kTile;        // K tile + V tile
@@ -69,7 +80,7 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, (kQT >= 4 || kWaves > 4) ? 1 : 2)
 attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, float* __restrict__ lse,
                 int S, int heads, int nqt, float scale_log2) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
@@ -87,10 +98,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
 
   // Q fragments (B operand of S^T = K Q^T): query 16u + l16 of this wave,
   // channels 32k + 8*grp .. +7.
-  const int q0 = qt * kBM + wave * 32;
-  bf16x8_t qf[2][4];
+  const int q0 = qt * kBM + wave * 16 * kQT;
+  bf16x8_t qf[kQT][4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kQT; ++u) {
     int q = q0 + 16 * u + l16;
     q = q < S ? q : S - 1;
     const uint16_t* qp = base + (int64_t)q * rs + 8 * grp;
@@ -98,21 +109,26 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
     for (int k = 0; k < 4; ++k) qf[u][k] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * k);
   }
 
-  f32x4_t acc_o[8][2];
+  f32x4_t acc_o[8][kQT];
+  float m_run[kQT], l_run[kQT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc_o[i][0] = acc_o[i][1] = f32x4_t{};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  for (int u = 0; u < kQT; ++u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc_o[i][u] = f32x4_t{};
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+  }
 
   // Direct global -> LDS staging: lane l of a wave instruction lands at the
-  // wave-uniform LDS base + 16*l. Each wave fills four 1 KB blocks (4 rows) of
-  // the K tile and of the V tile; lane l of a block takes physical row
+  // wave-uniform LDS base + 16*l. Each wave fills 16/kWaves 1 KB blocks (4 rows)
+  // of the K tile and of the V tile; lane l of a block takes physical row
   // 4*blk + l/16, physical chunk l%16, and fetches the logical chunk the
   // swizzle maps there. Rows past the end re-read row S-1 (masked later).
   auto issue_tile = [&](int k0, int stage) {
     unsigned char* ks = smem + stage * kStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = 4 * wave + j;
+    for (int j = 0; j < 16 / kWaves; ++j) {
+      const int blk = (16 / kWaves) * wave + j;
       const int r = 4 * blk + (lane >> 4), pc = lane & 15;
       const uint16_t* rp = base + (int64_t)min(k0 + r, S - 1) * rs;
       __builtin_amdgcn_global_load_lds(rp + D + 8 * (pc ^ k_xor(r)), ks + blk * 1024, 16, 0, 0);
@@ -137,16 +153,17 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
     if (kt + 1 < nkt) issue_tile(k0 + kBN, (kt + 1) & 1);
 
     // S^T: 4 key tiles (16 keys) x 2 query tiles, K over the 128 channels.
-    f32x4_t acc_s[4][2];
+    f32x4_t acc_s[4][kQT];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      acc_s[t][0] = acc_s[t][1] = f32x4_t{};
+#pragma unroll
+      for (int u = 0; u < kQT; ++u) acc_s[t][u] = f32x4_t{};
       const int r = 16 * t + l16;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + r * kRow + 16 * ((4 * k + grp) ^ k_xor(r)));
-        acc_s[t][0] = mfma16(a, qf[0][k], acc_s[t][0]);
-        acc_s[t][1] = mfma16(a, qf[1][k], acc_s[t][1]);
+#pragma unroll
+        for (int u = 0; u < kQT; ++u) acc_s[t][u] = mfma16(a, qf[u][k], acc_s[t][u]);
       }
     }
 
@@ -156,13 +173,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (k0 + 16 * t + 4 * grp + i >= S) acc_s[t][0][i] = acc_s[t][1][i] = -INFINITY;
+          if (k0 + 16 * t + 4 * grp + i >= S) {
+#pragma unroll
+            for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
+          }
     }
 
     // Online softmax per query column (base-2, scale folded in), lazily rescaled.
-    bf16x8_t pf[2][2];
+    bf16x8_t pf[kQT][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kQT; ++u) {
       float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
 #pragma unroll
       for (int t = 1; t < 4; ++t)
@@ -204,8 +224,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
         const s16x4_t lo = lds_read_tr16(vs + r0 * kRow + 16 * (ch ^ v_xor(r0)) + sub);
         const s16x4_t hi4 = lds_read_tr16(vs + r1 * kRow + 16 * (ch ^ v_xor(r1)) + sub);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[dt][0] = mfma16(a, pf[0][c], acc_o[dt][0]);
-        acc_o[dt][1] = mfma16(a, pf[1][c], acc_o[dt][1]);
+#pragma unroll
+        for (int u = 0; u < kQT; ++u) acc_o[dt][u] = mfma16(a, pf[u][c], acc_o[dt][u]);
       }
     }
 
@@ -215,7 +235,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
 
   // Epilogue: O = O^T / l in bf16; lane holds 4 consecutive channels per (dt, u).
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kQT; ++u) {
     float l_tot = l_run[u] + __shfl_xor(l_run[u], 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     const int q = q0 + 16 * u + l16;

@@ -37,8 +37,13 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + i * blockDim.x;
     if (c < nchunks) {
+#if WAN_NORM_NT & 1
+      qv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(qrow + 8 * c));
+      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + 8 * c));
+#else
       qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * c);
       kv[i] = *reinterpret_cast<const u32x4_t*>(krow + 8 * c);
+#endif
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float a = bf16_lo(qv[i][j]), b = bf16_hi(qv[i][j]);
@@ -95,8 +100,13 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
         b = bf16_hi(nk);
         ko[j] = pack_bf16x2(a * cs.x - b * cs.y, a * cs.y + b * cs.x);
       }
+#if WAN_NORM_NT & 2
+      __builtin_nontemporal_store(qo, reinterpret_cast<u32x4_t*>(qrow + 8 * c));
+      __builtin_nontemporal_store(ko, reinterpret_cast<u32x4_t*>(krow + 8 * c));
+#else
       *reinterpret_cast<u32x4_t*>(qrow + 8 * c) = qo;
       *reinterpret_cast<u32x4_t*>(krow + 8 * c) = ko;
+#endif
     }
   }
 }
@@ -106,8 +116,15 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
 hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const float2* tab,
                               int64_t row0, int64_t rows, int S, int T, int H, int W, int D,
                               float eps, hipStream_t stream) {
+#ifndef WAN_NORM_MIN_CPT
+#define WAN_NORM_MIN_CPT 2  // two 16-byte chunks of Q and of K per thread: more bytes in flight per CU
+#endif
+#ifndef WAN_NORM_NT
+#define WAN_NORM_NT 3  // non-temporal loads (1) and stores (2): the rows are touched once
+#endif
   const int nchunks = D / 8;
-  const int cpt = nchunks <= 1024 ? 1 : (nchunks <= 2048 ? 2 : 4);
+  int cpt = nchunks <= 1024 ? 1 : (nchunks <= 2048 ? 2 : 4);
+  cpt = cpt < WAN_NORM_MIN_CPT ? WAN_NORM_MIN_CPT : cpt;
   const int per = (nchunks + cpt - 1) / cpt;
   const int threads = ((per + 63) / 64) * 64;
   const int offH = T * kPairsT, offW = offH + H * kPairsH;
