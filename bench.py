@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "720p_fp8", "long", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, run one plain device copy of MIB MiB (its hardware "
+                         "counters scale FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
@@ -127,6 +130,13 @@ def main():
             wan_attn.attn_fwd(qkv, w.heads, out=out)
         if ev: ev[3].record(stream)
 
+    if args.copy_calibration:
+        n = args.copy_calibration * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
