@@ -9,8 +9,13 @@
 // buffer, V transposed per head [B, heads, 128, S_pad] e4m3, and the three
 // per-tensor scales (x8 = x * scale). Scores are q8 . k8 / (scale_q scale_k)
 // * softmax_scale; the softmax is fp32 (base 2, scale folded in); P is
-// quantised to e4m3 at a fixed scale of 2^8 and the output is
-// (sum p8 v8) / (2^8 * scale_v * l), with l the fp32 sum of P.
+// quantised to e4m3 at a fixed scale of 2^8 (folded into the exponent:
+// p8 = e4m3(exp2(s - m + 8))) and the output is (sum p8 v8) / (scale_v * l8),
+// with l8 = sum p8 accumulated by the MFMA itself: one extra 16x16x128 MFMA per
+// query tile multiplies P by a constant operand whose first row is all ones,
+// which costs 1/16 more MFMA work and removes a VALU add per score (the
+// softmax, not the MFMA, bounds this kernel), and normalises by exactly the
+// quantised weights used in PV.
 //
 // Work decomposition (same skeleton as the bf16 kernel):
 //   * workgroup = 4 waves = 128 queries of one (b, h); each wave owns 32 queries
@@ -36,13 +41,17 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kBN = 128;                 // keys per unit
-constexpr int kWaves = 4;
+#ifndef WAN_FP8_WAVES
+#define WAN_FP8_WAVES 4
+#endif
+constexpr int kWaves = WAN_FP8_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;
 constexpr int kTile = 128 * 128;         // bytes of one K or V^T tile
 constexpr int kStage = 2 * kTile;
-constexpr float kPScale = 256.0f;        // P is quantised as e4m3(p * 2^8)
+constexpr float kPLog2Scale = 8.0f;      // P is quantised as e4m3(p * 2^8)
 constexpr float kRescaleSlack = 0.75f;   // keeps p * 2^8 <= 2^8.75 < 448
+constexpr int kE4m3One = 0x38383838;     // four e4m3 1.0 bytes
 
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   const int xcd = bid & 7, j = bid >> 3;
@@ -64,7 +73,7 @@ __device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, kWaves > 4 ? 1 : 2)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__ vt8,
                     const float* __restrict__ scales, uint16_t* __restrict__ out, float* __restrict__ lse, int S,
                     int S_pad, int heads, int nqt, float softmax_scale) {
@@ -97,10 +106,15 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
     qf[u] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
   }
 
-  f32x4_t acc_o[8][2];
+  f32x4_t acc_o[8][2], acc_l[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc_o[i][0] = acc_o[i][1] = f32x4_t{};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  acc_l[0] = acc_l[1] = f32x4_t{};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  // A operand whose row 0 is all ones (rows 1..15 zero): row 0 of ones x P^T is
+  // the column sum of P, i.e. l for each query, in lane (grp 0, l16), register 0.
+  const int one = l16 == 0 ? kE4m3One : 0;
+  const i32x8_t ones = {one, one, one, one, one, one, one, one};
 
   // Direct global -> LDS staging (global_load_lds_dwordx4: lane l of a wave
   // instruction lands at the wave-uniform LDS base + 16*l). Each wave fills four
@@ -110,8 +124,8 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
   auto issue_unit = [&](int k0, int stage) {
     unsigned char* ks = smem + stage * kStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = 4 * wave + j;
+    for (int j = 0; j < 16 / kWaves; ++j) {
+      const int blk = (16 / kWaves) * wave + j;
       const int r = 8 * blk + (lane >> 3), pc = lane & 7;
       const int key = min(k0 + r, S - 1);
       __builtin_amdgcn_global_load_lds(qkb + (int64_t)key * rs + D + 16 * (pc ^ k_xor(r)), ks + blk * 1024, 16, 0, 0);
@@ -166,26 +180,24 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
         const float m_new = fmaxf(m_run[u], mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
         m_run[u] = m_new;
-        l_run[u] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_l[u][i] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
       }
-      float psum = 0.f;
+      const float m_shift = m_run[u] - kPLog2Scale;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(acc_s[t][u][i], c_log2, -m_run[u]));
-          psum += p[i];
-        }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * kPScale, p[1] * kPScale, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * kPScale, p[3] * kPScale, w, true);
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(acc_s[t][u][i], c_log2, -m_shift));
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pf[u][t] = w;
       }
-      l_run[u] += psum;
+      acc_l[u] = mfma_fp8(ones, pf[u], acc_l[u]);
     }
 
     // O^T += V^T P^T: 8 channel tiles, K = the 128 keys of the unit.
@@ -203,14 +215,12 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
     __syncthreads();                          // ... and every other wave's; this stage is free
   }
 
-  const float out_scale = dv / kPScale;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    float l_tot = l_run[u] + __shfl_xor(l_run[u], 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = __shfl(acc_l[u][0], l16, 64);  // l8 of query l16 lives in lane l16
     const int q = q0 + 16 * u + l16;
     if (q < S) {
-      const float inv = out_scale / l_tot;
+      const float inv = dv / l_tot;
       uint16_t* op = out + ((int64_t)b * S + q) * D + h * kD + 4 * grp;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -219,7 +229,8 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
         w.y = pack_bf16x2(acc_o[dt][u][2] * inv, acc_o[dt][u][3] * inv);
         *reinterpret_cast<uint2*>(op + 16 * dt) = w;
       }
-      if (lse && grp == 0) lse[(int64_t)bh * S + q] = (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f;
+      // l8 = 2^8 * sum p, so ln(sum exp(s)) = (m + log2(l8) - 8) * ln 2
+      if (lse && grp == 0) lse[(int64_t)bh * S + q] = (m_run[u] + __log2f(l_tot) - kPLog2Scale) * 0.69314718055994531f;
     }
   }
 }
