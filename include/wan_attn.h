@@ -127,7 +127,8 @@ int wan_qknorm_rope(void *qkv, const void *gamma_q, const void *gamma_k,
  *   out[b, s, h*128 + i] = sum_t p(s,t) V[b,t,h,i],
  *   p(s,t) = softmax_t( Q[b,s,h,:] . K[b,t,h,:] * softmax_scale )
  * over every key t < S; no mask, no dropout. QK^T and PV run on bf16 MFMA with
- * fp32 accumulation; the softmax is fp32; P is rounded to bf16 for PV.
+ * fp32 accumulation; the softmax is fp32; P is rounded to bf16 for PV and the
+ * row sum that normalises the output is the fp32 sum of those bf16 weights.
  *
  *   qkv            bf16 [B, S, 3*D] packed buffer (normally after
  *                  wan_qknorm_rope); read only.
@@ -182,8 +183,8 @@ int64_t wan_fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim);
  * wan_attn_fwd_fp8 -- bidirectional attention from the wan_qkv_quant_fp8
  * buffers on fp8 MFMA (16x16x128 e4m3, fp32 accumulation):
  *   s     = (q8 . k8) / (scale_q * scale_k) * softmax_scale      (fp32)
- *   p     = softmax over all S keys (fp32, online)
- *   out   = sum_t e4m3(p * 2^8) v8 / (2^8 * scale_v * l),  l = fp32 sum of p
+ *   p8    = e4m3(2^8 * exp(s - m)), m a running maximum (fp32 softmax, online)
+ *   out   = sum_t p8 v8 / (scale_v * sum_t p8)
  *
  *   qk8, vt8, scales  as written by wan_qkv_quant_fp8 for the same sizes.
  *   out               bf16 [B, S, D]; must not overlap the inputs.

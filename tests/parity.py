@@ -75,7 +75,11 @@ def attn_error_stats(gpu, ref):
 # stay meaningful when the output magnitude shrinks as 1/sqrt(S).
 BF16_GATES = {"max": 2e-2, "mean": 2e-3, "rel_l2": 1e-2, "cos": 0.9999}
 FP8_GATES = {"max": 6e-2, "rel_l2": 5e-2, "cos": 0.999}
-LSE_ABS = 1e-3
+# The kernel's softmax denominator is the sum of the bf16-rounded weights PV
+# uses (each within 2^-8 relative of the exact weight), so ln(l) -- and the LSE
+# -- may differ from the exact value by up to ln(1 + 2^-8) = 3.9e-3 when one
+# weight dominates; the gate leaves a margin above that.
+LSE_ABS = 5e-3
 
 
 def assert_gates(stats, gates, what=""):

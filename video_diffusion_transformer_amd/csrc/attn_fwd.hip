@@ -33,7 +33,8 @@
 //     rows one lane group reads, and the 8 V rows x 32 B half a wave reads with
 //     the transposing load, fall in distinct banks;
 //   * the O^T accumulator keeps one query column per lane, so the rescale by
-//     exp2(m_old - m_new) is lane-local. The running max only moves when a
+//     exp2(m_old - m_new) is lane-local, and the row sums of P are accumulated
+//     by one extra MFMA against a row of ones. The running max only moves when a
 //     tile's max exceeds it by more than 8 (log2 units): most tiles skip the
 //     rescale; the stale max keeps p <= 2^8 (exact in fp32, far from bf16
 //     overflow) and the final normalisation uses the same max, so the result is
@@ -109,14 +110,22 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
     for (int k = 0; k < 4; ++k) qf[u][k] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * k);
   }
 
-  f32x4_t acc_o[8][kQT];
-  float m_run[kQT], l_run[kQT];
+  // Row sums of P come from the MFMA too: an A operand whose row 0 is all
+  // bf16 ones (rows 1..15 zero) times P^T gives, in register 0 of lane l16 of
+  // lane group 0, the sum of the bf16 probabilities of query l16 -- one extra
+  // MFMA per 32 keys instead of a VALU add per score, and the normalisation uses
+  // exactly the weights PV used.
+  f32x4_t acc_o[8][kQT], acc_l[kQT];
+  float m_run[kQT];
+  const unsigned short one = l16 == 0 ? 0x3f80 : 0;
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, s16x8_t{(short)one, (short)one, (short)one, (short)one,
+                                                              (short)one, (short)one, (short)one, (short)one});
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc_o[i][u] = f32x4_t{};
+    acc_l[u] = f32x4_t{};
     m_run[u] = -INFINITY;
-    l_run[u] = 0.f;
   }
 
   // Direct global -> LDS staging: lane l of a wave instruction lands at the
@@ -193,25 +202,22 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
         const float m_new = fmaxf(m_run[u], mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
         m_run[u] = m_new;
-        l_run[u] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_l[u][i] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
       }
-      float psum = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8_t v;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], scale_log2, -m_run[u]));
-          psum += p;
-          v[j] = (__bf16)p;
-        }
+        for (int j = 0; j < 8; ++j)
+          v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], scale_log2, -m_run[u]));
         pf[u][c] = v;
+        acc_l[u] = mfma16(ones, v, acc_l[u]);
       }
-      l_run[u] += psum;
     }
 
     // O^T (channels x queries) += V^T P^T: 8 channel tiles x 2 key steps of 32.
@@ -236,8 +242,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
   // Epilogue: O = O^T / l in bf16; lane holds 4 consecutive channels per (dt, u).
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
-    float l_tot = l_run[u] + __shfl_xor(l_run[u], 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = __shfl(acc_l[u][0], l16, 64);  // sum of the bf16 P of query l16, in lane l16
     const int q = q0 + 16 * u + l16;
     if (q < S) {
       const float inv = 1.0f / l_tot;
