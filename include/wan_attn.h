@@ -146,6 +146,44 @@ int wan_attn_fwd(const void *qkv, void *out, float *lse,
                  float softmax_scale, void *stream);
 
 /*
+ * wan_attn_fwd_chunk -- one round of ring attention on one device ("Optimizing
+ * High-Quality Offline Video Generation", Context parallelism: each rank keeps
+ * its S/CP queries and K/V chunks rotate around the ring so the local queries
+ * attend the whole sequence). The local queries attend ONE chunk of keys and
+ * values; the result is normalised within the chunk and returned with its
+ * log-sum-exp, ready for wan_attn_merge.
+ *
+ *   q_src      bf16 [B, Sq, 3*D] packed buffer; its Q part holds the queries.
+ *   kv_src     bf16 [B, Skv, 3*D] packed buffer; its K and V parts hold the
+ *              chunk (may be q_src itself). Both read only.
+ *   out        fp32 [B, Sq, D]: softmax over the chunk's keys times its values.
+ *   lse        fp32 [B, heads, Sq]: natural log-sum-exp of the chunk's scores
+ *              (required).
+ * Sq == 0 or B == 0 is a no-op; Skv must be >= 1 when there are queries.
+ * out and lse must not overlap the inputs or each other.
+ * Errors: as wan_attn_fwd (WAN_E_SHAPE also for Skv == 0).
+ */
+int wan_attn_fwd_chunk(const void *q_src, int64_t Sq, const void *kv_src, int64_t Skv,
+                       float *out, float *lse, int64_t B, int64_t heads, int64_t head_dim,
+                       float softmax_scale, void *stream);
+
+/*
+ * wan_attn_merge -- fold a chunk result into an accumulator of earlier chunks
+ * (disjoint key sets), in place:
+ *   L = log(exp(acc_lse) + exp(chunk_lse));
+ *   acc_out = exp(acc_lse - L) acc_out + exp(chunk_lse - L) chunk_out;  acc_lse = L
+ * An accumulator row with acc_lse = -inf counts as empty.
+ *   acc_out    fp32 [B, Sq, D] in/out;   acc_lse   fp32 [B, heads, Sq] in/out.
+ *   chunk_out  fp32 [B, Sq, D];          chunk_lse fp32 [B, heads, Sq].
+ *   out_bf16   bf16 [B, Sq, D] copy of the merged output, or NULL.
+ * No two buffers may overlap. Errors: WAN_E_NULL, WAN_E_SHAPE,
+ * WAN_E_UNSUPPORTED, WAN_E_ALIGN, WAN_E_ALIAS, WAN_E_OVERFLOW, WAN_E_HIP.
+ */
+int wan_attn_merge(float *acc_out, float *acc_lse, const float *chunk_out, const float *chunk_lse,
+                   void *out_bf16, int64_t B, int64_t Sq, int64_t heads, int64_t head_dim,
+                   void *stream);
+
+/*
  * wan_qkv_quant_fp8 -- per-tensor e4m3 quantisation of Q, K and V for the fp8
  * attention path (the amax -> E4M3 scale -> quantise recipe of "Optimize Wan2.2
  * Dataflow", change 2, applied to the attention inputs; the pull request's

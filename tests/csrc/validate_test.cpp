@@ -70,6 +70,41 @@ int main() {
   EXPECT_EQ(validate_attn(qkv, outb, nullptr, 1, (int64_t)INT32_MAX + 1, 2, 128, 0.088f, 2, &z), WAN_E_OVERFLOW);
   EXPECT_EQ(validate_attn(qkv, outb, nullptr, -2, 16, 2, 128, 0.088f, 2, &z), WAN_E_SHAPE);
 
+  // chunk + merge
+  alignas(16) static float of32[1 << 14];
+  alignas(16) static float lsea[256], lsec[256];
+  alignas(16) static float of32b[1 << 14];
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, lsea, 1, 16, 16, 2, 128, 0.088f, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, nullptr, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, lsea, 1, 16, 0, 2, 128, 0.088f, &z), WAN_E_SHAPE);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, lsea, 1, 0, 0, 2, 128, 0.088f, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, buf + 1024, lsea, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, of32 + 4, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, lsea, 1, 16, -1, 2, 128, 0.088f, &z), WAN_E_SHAPE);
+  EXPECT_EQ(validate_attn_merge(of32, lsea, of32b, lsec, nullptr, 1, 16, 2, 128, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_merge(of32, lsea, of32b, lsec, outb, 1, 16, 2, 128, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_merge(of32, lsea, of32, lsec, nullptr, 1, 16, 2, 128, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_merge(of32, lsea, of32b, lsea, nullptr, 1, 16, 2, 128, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_merge(of32, lsea, of32b, nullptr, nullptr, 1, 16, 2, 128, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_attn_merge(of32 + 1, lsea, of32b, lsec, nullptr, 1, 16, 2, 128, &z), WAN_E_ALIGN);
+
+  // fp8 quantisation and attention
+  alignas(16) static unsigned char qk8[1 << 16], vt8[1 << 16];
+  alignas(16) static float sc[4], am[4];
+  EXPECT_EQ(validate_quant_fp8(qkv, qk8, vt8, sc, am, 1, 16, 2, 128, &z), WAN_OK);
+  EXPECT_EQ(validate_quant_fp8(qkv, qk8, vt8, sc, sc, 1, 16, 2, 128, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_quant_fp8(qkv, qk8, qk8 + 16, sc, am, 1, 16, 2, 128, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_quant_fp8(qkv, buf + 512, vt8, sc, am, 1, 16, 2, 128, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_quant_fp8(qkv, qk8, vt8, sc, am, 70000, 16, 2, 128, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_quant_fp8(qkv, qk8, nullptr, sc, am, 1, 16, 2, 128, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_attn_fp8(qk8, vt8, sc, outb, lsea, 1, 16, 2, 128, 0.088f, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_fp8(qk8, vt8, sc, qk8 + 64, nullptr, 1, 16, 2, 128, 0.088f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_fp8(qk8, vt8, nullptr, outb, nullptr, 1, 16, 2, 128, 0.088f, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_attn_fp8(qk8, vt8, sc, outb, nullptr, 1, 16, 2, 128, -2.f, &z), WAN_E_VALUE);
+  int64_t vtb = 0;
+  EXPECT_EQ(fp8_vt_bytes(2, 129, 3, &vtb), 1);
+  EXPECT_EQ(vtb, 2 * 3 * 128 * 256);
+
   if (failures) {
     std::fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -1,0 +1,102 @@
+"""GPU parity of the ring-attention building blocks (wan_attn_fwd_chunk,
+wan_attn_merge): queries attend K/V chunks one at a time and the partial
+results are merged by their log-sum-exp; the merged result must match the
+oracle's full attention, and each chunk the oracle's chunk attention."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import wan_ref
+from tests.parity import BF16_GATES, LSE_ABS, assert_gates, attn_error_stats
+from video_diffusion_transformer_amd import synth, wan_attn
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SCALE = 1.0 / math.sqrt(128.0)
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _ring(q_src, kv_full, heads, bounds, order=None):
+    """Attend q_src to the K/V chunks kv_full[:, a:b] and merge them."""
+    B, Sq = q_src.shape[0], q_src.shape[1]
+    D = heads * 128
+    acc = torch.zeros((B, Sq, D), dtype=torch.float32, device=DEV)
+    acc_lse = torch.full((B, heads, Sq), -math.inf, dtype=torch.float32, device=DEV)
+    out16 = torch.empty((B, Sq, D), dtype=torch.bfloat16, device=DEV)
+    chunks = list(zip(bounds[:-1], bounds[1:]))
+    for i in (order or range(len(chunks))):
+        a, b = chunks[i]
+        kv = kv_full[:, a:b].contiguous()
+        o, l = wan_attn.attn_fwd_chunk(q_src, kv, heads)
+        wan_attn.attn_merge(acc, acc_lse, o, l, heads, out_bf16=out16)
+    torch.cuda.synchronize()
+    return acc, acc_lse, out16
+
+
+@pytest.mark.parametrize("B,S,heads,bounds", [(1, 500, 2, [0, 130, 333, 500]), (2, 777, 3, [0, 1, 400, 777]),
+                                              (1, 300, 40, [0, 150, 300]), (1, 1000, 2, [0, 64, 128, 640, 1000])])
+def test_ring_merge_equals_full_attention(B, S, heads, bounds):
+    qkv = synth.make_qkv(B, S, heads, seed=S + heads).to(DEV)
+    acc, acc_lse, out16 = _ring(qkv, qkv, heads, bounds)
+    o_ref, l_ref = wan_ref.attn_packed_ref(_np(qkv), heads, 128, SCALE)
+    assert_gates(attn_error_stats(_np(out16), o_ref), BF16_GATES, "merged bf16")
+    st = attn_error_stats(_np(acc), o_ref)
+    assert st["rel_l2"] <= 5e-3 and st["max"] <= 1e-2, st
+    assert np.abs(_np(acc_lse) - l_ref).max() <= LSE_ABS
+
+
+def test_query_shard_against_chunks_and_order():
+    """A contiguous query shard (as one ring rank holds) against chunks merged
+    in two different orders."""
+    B, S, heads = 1, 900, 2
+    D = heads * 128
+    qkv = synth.make_qkv(B, S, heads, seed=31).to(DEV)
+    shard = qkv[:, 300:600].contiguous()
+    bounds = [0, 300, 600, 900]
+    a, la, oa = _ring(shard, qkv, heads, bounds, order=[1, 0, 2])
+    b, lb, ob = _ring(shard, qkv, heads, bounds, order=[2, 1, 0])
+    o_ref, l_ref = wan_ref.attn_packed_ref(_np(qkv), heads, 128, SCALE, rows=np.arange(300, 600))
+    for acc, lse, o16 in ((a, la, oa), (b, lb, ob)):
+        assert_gates(attn_error_stats(_np(o16), o_ref), BF16_GATES, "shard")
+        assert np.abs(_np(lse) - l_ref).max() <= LSE_ABS
+    assert (a - b).abs().max().item() <= 1e-5
+
+
+def test_chunk_matches_oracle_chunk_and_full_kernel():
+    B, S, heads = 2, 333, 2
+    D = heads * 128
+    qkv = synth.make_qkv(B, S, heads, seed=32).to(DEV)
+    kv = qkv[:, 100:250].contiguous()
+    o, l = wan_attn.attn_fwd_chunk(qkv, kv, heads)
+    torch.cuda.synchronize()
+    host = _np(qkv)
+    for b in range(B):
+        for h in range(heads):
+            c = slice(h * 128, (h + 1) * 128)
+            ref, lref = wan_ref.attn_chunk_ref(host[b, :, c], host[b, 100:250, D + h * 128:D + (h + 1) * 128],
+                                               host[b, 100:250, 2 * D + h * 128:2 * D + (h + 1) * 128], SCALE)
+            assert_gates(attn_error_stats(_np(o[b, :, c]), ref), BF16_GATES, f"chunk b{b} h{h}")
+            assert np.abs(_np(l[b, h]) - lref).max() <= LSE_ABS
+    # the whole sequence as one chunk is the full kernel, before its bf16 rounding
+    full_f32, _ = wan_attn.attn_fwd_chunk(qkv, qkv, heads)
+    full_bf16 = wan_attn.attn_fwd(qkv, heads)
+    torch.cuda.synchronize()
+    assert torch.equal(full_f32.to(torch.bfloat16), full_bf16)
+
+
+def test_chunk_errors():
+    q = torch.zeros((1, 8, 768), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(wan_attn.WanError) as e:
+        wan_attn.attn_fwd_chunk(q, torch.zeros((1, 0, 768), dtype=torch.bfloat16, device=DEV), 2)
+    assert e.value.status == -2
+    o, l = wan_attn.attn_fwd_chunk(q, q, 2)
+    with pytest.raises(wan_attn.WanError) as e:  # merging a buffer into itself
+        wan_attn.attn_merge(o, l, o, l, 2)
+    assert e.value.status == -5

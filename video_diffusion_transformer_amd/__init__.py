@@ -5,6 +5,6 @@ C ABI in include/wan_attn.h); this package holds the ctypes binding, the build
 script, the workload definitions and the seeded input generators.
 """
 
-from .wan_attn import (Fp8QKV, WanError, attn_fwd, attn_fwd_fp8, fp8_buffers, lib, qkv_quant_fp8,  # noqa: F401
-                       qknorm_rope, token_grid)
+from .wan_attn import (Fp8QKV, WanError, attn_fwd, attn_fwd_chunk, attn_fwd_fp8, attn_merge,  # noqa: F401
+                       fp8_buffers, lib, qkv_quant_fp8, qknorm_rope, token_grid)
 from .configs import WORKLOADS, Workload  # noqa: F401

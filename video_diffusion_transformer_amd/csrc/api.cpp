@@ -117,6 +117,31 @@ int wan_attn_fwd(const void* qkv, void* out, float* lse, int64_t B, int64_t S, i
   return WAN_OK;
 }
 
+int wan_attn_fwd_chunk(const void* q_src, int64_t Sq, const void* kv_src, int64_t Skv, float* out, float* lse,
+                       int64_t B, int64_t heads, int64_t head_dim, float softmax_scale, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_attn_chunk(q_src, kv_src, out, lse, B, Sq, Skv, heads, head_dim, softmax_scale, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (B > INT32_MAX) return WAN_E_OVERFLOW;
+  if (wan::launch_attn_fwd_chunk(q_src, static_cast<int>(Sq), kv_src, static_cast<int>(Skv), out, lse,
+                                 static_cast<int>(B), static_cast<int>(heads), softmax_scale,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
+int wan_attn_merge(float* acc_out, float* acc_lse, const float* chunk_out, const float* chunk_lse, void* out_bf16,
+                   int64_t B, int64_t Sq, int64_t heads, int64_t head_dim, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_attn_merge(acc_out, acc_lse, chunk_out, chunk_lse, out_bf16, B, Sq, heads, head_dim, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (B > INT32_MAX) return WAN_E_OVERFLOW;
+  if (wan::launch_attn_merge(acc_out, acc_lse, chunk_out, chunk_lse, out_bf16, static_cast<int>(B), static_cast<int>(Sq),
+                             static_cast<int>(heads), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
 int wan_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int64_t B, int64_t S,
                       int64_t heads, int64_t head_dim, void* stream) {
   wan::Sizes z;

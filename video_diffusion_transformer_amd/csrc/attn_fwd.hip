@@ -81,9 +81,132 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Per-kernel constants shared by the tile step below.
+struct TileArgs {
+  const uint16_t* base;  // K/V rows of this (b, h): element offset of channel 0 of row 0
+  int S, rs, D, nkt, wave, lane, l16, grp, vr;
+  float scale_log2;
+};
+
+// Direct global -> LDS staging of one 64-key tile: lane l of a wave
+// instruction lands at the wave-uniform LDS base + 16*l. Each wave fills
+// 16/kWaves 1 KB blocks (4 rows) of the K tile and of the V tile; lane l of a
+// block takes physical row 4*blk + l/16, physical chunk l%16, and fetches the
+// logical chunk the swizzle maps there. Rows past the end re-read row S-1
+// (masked later).
+__device__ __forceinline__ void issue_tile(const TileArgs& a, int k0, unsigned char* __restrict__ ks) {
+#pragma unroll
+  for (int j = 0; j < 16 / kWaves; ++j) {
+    const int blk = (16 / kWaves) * a.wave + j;
+    const int r = 4 * blk + (a.lane >> 4), pc = a.lane & 15;
+    const uint16_t* rp = a.base + (int64_t)min(k0 + r, a.S - 1) * a.rs;
+    __builtin_amdgcn_global_load_lds(rp + a.D + 8 * (pc ^ k_xor(r)), ks + blk * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rp + 2 * a.D + 8 * (pc ^ v_xor(r)), ks + kTile + blk * 1024, 16, 0, 0);
+  }
+}
+
+// One 64-key tile: scores, online softmax and PV from stage `cur`, while the
+// next tile streams into stage `nxt`.
+__device__ __forceinline__ void tile_step(const TileArgs& a, int kt, const unsigned char* __restrict__ cur,
+                                          unsigned char* __restrict__ nxt, const bf16x8_t (&qf)[kQT][4],
+                                          f32x4_t (&acc_o)[8][kQT], f32x4_t (&acc_l)[kQT], float (&m_run)[kQT],
+                                          const bf16x8_t& ones) {
+  const int k0 = kt * kBN;
+  const unsigned char* ks = cur;
+  const unsigned char* vs = cur + kTile;
+  // The other stage was last read in iteration kt-1, which every wave has left.
+  if (kt + 1 < a.nkt) issue_tile(a, k0 + kBN, nxt);
+
+  // S^T: 4 key tiles (16 keys) x kQT query tiles, K over the 128 channels.
+  f32x4_t acc_s[4][kQT];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int u = 0; u < kQT; ++u) acc_s[t][u] = f32x4_t{};
+    const int r = 16 * t + a.l16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ks + r * kRow + 16 * ((4 * k + a.grp) ^ k_xor(r)));
+#pragma unroll
+      for (int u = 0; u < kQT; ++u) acc_s[t][u] = mfma16(av, qf[u][k], acc_s[t][u]);
+    }
+  }
+
+  // Mask keys past the end (only the last tile can have them).
+  if (k0 + kBN > a.S) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + 16 * t + 4 * a.grp + i >= a.S) {
+#pragma unroll
+          for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
+        }
+  }
+
+  // Online softmax per query column (base-2, scale folded in), lazily rescaled.
+  bf16x8_t pf[kQT][2];
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) {
+    float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
+#pragma unroll
+    for (int t = 1; t < 4; ++t)
+      mx = fmaxf(mx, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+    if (__ballot(mx > m_run[u] + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run[u], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
+      m_run[u] = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_l[u][i] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8_t v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], a.scale_log2, -m_run[u]));
+      pf[u][c] = v;
+      acc_l[u] = mfma16(ones, v, acc_l[u]);
+    }
+  }
+
+  // Let the next tile's direct-to-LDS writes finish before the transposed V
+  // reads: measured, the PV phase runs faster without those writes competing
+  // for the LDS, and the loads have had the score and softmax phases to land.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  // O^T (channels x queries) += V^T P^T: 8 channel tiles x 2 key steps of 32.
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int ch = 2 * dt + ((a.l16 & 3) >> 1), sub = 8 * (a.l16 & 1);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r0 = 32 * c + a.vr, r1 = r0 + 16;
+      const s16x4_t lo = lds_read_tr16(vs + r0 * kRow + 16 * (ch ^ v_xor(r0)) + sub);
+      const s16x4_t hi4 = lds_read_tr16(vs + r1 * kRow + 16 * (ch ^ v_xor(r1)) + sub);
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int u = 0; u < kQT; ++u) acc_o[dt][u] = mfma16(av, pf[u][c], acc_o[dt][u]);
+    }
+  }
+
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
+  __syncthreads();                          // ... and every wave's; stage `cur` is free again
+}
+
+// Queries come from the Q part of one packed buffer (Sq rows per batch entry),
+// keys and values from the K and V parts of another (Skv rows); for full
+// attention both are the same buffer. F32Out selects an fp32 output (the
+// chunked path, whose partial outputs are merged later) instead of bf16.
+template <bool F32Out>
 __global__ void __launch_bounds__(kThreads, (kQT >= 4 || kWaves > 4) ? 1 : 2)
-attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, float* __restrict__ lse,
-                int S, int heads, int nqt, float scale_log2) {
+attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ kvsrc, void* __restrict__ out,
+                float* __restrict__ lse, int Sq, int S, int heads, int nqt, float scale_log2) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -92,23 +215,43 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
   const int h = bh % heads, b = bh / heads;
   const int D = heads * kD;
   const int rs = 3 * D;  // row stride in elements (< 2^17)
-  const uint16_t* base = qkv + (int64_t)b * S * rs + h * kD;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
+  TileArgs a;
+  a.base = kvsrc + (int64_t)b * S * rs + h * kD;
+  a.S = S;
+  a.rs = rs;
+  a.D = D;
+  a.nkt = (S + kBN - 1) / kBN;
+  a.wave = wave;
+  a.lane = lane;
+  a.l16 = l16;
+  a.grp = grp;
+  a.vr = 4 * grp + (l16 >> 2);  // V^T source row 4*grp + l16/4 (+32c, +16)
+  a.scale_log2 = scale_log2;
 
   // Q fragments (B operand of S^T = K Q^T): query 16u + l16 of this wave,
   // channels 32k + 8*grp .. +7.
+  const uint16_t* qbase = qsrc + (int64_t)b * Sq * rs + h * kD;
   const int q0 = qt * kBM + wave * 16 * kQT;
   bf16x8_t qf[kQT][4];
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
     int q = q0 + 16 * u + l16;
-    q = q < S ? q : S - 1;
-    const uint16_t* qp = base + (int64_t)q * rs + 8 * grp;
+    q = q < Sq ? q : Sq - 1;
+    const uint16_t* qp = qbase + (int64_t)q * rs + 8 * grp;
 #pragma unroll
     for (int k = 0; k < 4; ++k) qf[u][k] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * k);
   }
+  // Complete the Q loads here: if they were still in flight at the loop head,
+  // the wait for them would land inside the loop, where it would also wait for
+  // the next tile's direct-to-LDS loads in every iteration. An empty asm that
+  // reads every fragment pins the loads (and their wait) to this block.
+#pragma unroll
+  for (int u = 0; u < kQT; ++u)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("" ::"v"(qf[u][k]));
 
   // Row sums of P come from the MFMA too: an A operand whose row 0 is all
   // bf16 ones (rows 1..15 zero) times P^T gives, in register 0 of lane l16 of
@@ -128,133 +271,38 @@ attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, fl
     m_run[u] = -INFINITY;
   }
 
-  // Direct global -> LDS staging: lane l of a wave instruction lands at the
-  // wave-uniform LDS base + 16*l. Each wave fills 16/kWaves 1 KB blocks (4 rows)
-  // of the K tile and of the V tile; lane l of a block takes physical row
-  // 4*blk + l/16, physical chunk l%16, and fetches the logical chunk the
-  // swizzle maps there. Rows past the end re-read row S-1 (masked later).
-  auto issue_tile = [&](int k0, int stage) {
-    unsigned char* ks = smem + stage * kStage;
-#pragma unroll
-    for (int j = 0; j < 16 / kWaves; ++j) {
-      const int blk = (16 / kWaves) * wave + j;
-      const int r = 4 * blk + (lane >> 4), pc = lane & 15;
-      const uint16_t* rp = base + (int64_t)min(k0 + r, S - 1) * rs;
-      __builtin_amdgcn_global_load_lds(rp + D + 8 * (pc ^ k_xor(r)), ks + blk * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(rp + 2 * D + 8 * (pc ^ v_xor(r)), ks + kTile + blk * 1024, 16, 0, 0);
-    }
-  };
-
-  // Per-lane LDS offsets: K A-operand row l16 (+16t), logical chunk 4k + grp;
-  // V^T source row 4*grp + l16/4 (+32c, +16), channels 32dt + 4*(l16%4).
-  const int vr = 4 * grp + (l16 >> 2);
-
-  const int nkt = (S + kBN - 1) / kBN;
-  issue_tile(0, 0);
+  issue_tile(a, 0, smem);
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * kBN;
-    const unsigned char* ks = smem + (kt & 1) * kStage;
-    const unsigned char* vs = ks + kTile;
-    // The other stage was last read in iteration kt-1, which every wave has left.
-    if (kt + 1 < nkt) issue_tile(k0 + kBN, (kt + 1) & 1);
-
-    // S^T: 4 key tiles (16 keys) x 2 query tiles, K over the 128 channels.
-    f32x4_t acc_s[4][kQT];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int u = 0; u < kQT; ++u) acc_s[t][u] = f32x4_t{};
-      const int r = 16 * t + l16;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + r * kRow + 16 * ((4 * k + grp) ^ k_xor(r)));
-#pragma unroll
-        for (int u = 0; u < kQT; ++u) acc_s[t][u] = mfma16(a, qf[u][k], acc_s[t][u]);
-      }
-    }
-
-    // Mask keys past the end (only the last tile can have them).
-    if (k0 + kBN > S) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + 16 * t + 4 * grp + i >= S) {
-#pragma unroll
-            for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
-          }
-    }
-
-    // Online softmax per query column (base-2, scale folded in), lazily rescaled.
-    bf16x8_t pf[kQT][2];
-#pragma unroll
-    for (int u = 0; u < kQT; ++u) {
-      float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
-#pragma unroll
-      for (int t = 1; t < 4; ++t)
-        mx = fmaxf(mx, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-      if (__ballot(mx > m_run[u] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run[u], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
-        m_run[u] = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc_l[u][i] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8_t v;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], scale_log2, -m_run[u]));
-        pf[u][c] = v;
-        acc_l[u] = mfma16(ones, v, acc_l[u]);
-      }
-    }
-
-    // O^T (channels x queries) += V^T P^T: 8 channel tiles x 2 key steps of 32.
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int ch = 2 * dt + ((l16 & 3) >> 1), sub = 8 * (l16 & 1);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r0 = 32 * c + vr, r1 = r0 + 16;
-        const s16x4_t lo = lds_read_tr16(vs + r0 * kRow + 16 * (ch ^ v_xor(r0)) + sub);
-        const s16x4_t hi4 = lds_read_tr16(vs + r1 * kRow + 16 * (ch ^ v_xor(r1)) + sub);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int u = 0; u < kQT; ++u) acc_o[dt][u] = mfma16(a, pf[u][c], acc_o[dt][u]);
-      }
-    }
-
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
-    __syncthreads();                          // ... and every wave's; stage kt&1 is free again
+  for (int kt = 0; kt < a.nkt; ++kt) {
+    unsigned char* cur = smem + (kt & 1) * kStage;
+    unsigned char* nxt = smem + ((kt + 1) & 1) * kStage;
+    tile_step(a, kt, cur, nxt, qf, acc_o, acc_l, m_run, ones);
   }
 
-  // Epilogue: O = O^T / l in bf16; lane holds 4 consecutive channels per (dt, u).
+  // Epilogue: O = O^T / l; lane holds 4 consecutive channels per (dt, u).
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
     const float l_tot = __shfl(acc_l[u][0], l16, 64);  // sum of the bf16 P of query l16, in lane l16
     const int q = q0 + 16 * u + l16;
-    if (q < S) {
+    if (q < Sq) {
       const float inv = 1.0f / l_tot;
-      uint16_t* op = out + ((int64_t)b * S + q) * D + h * kD + 4 * grp;
+      if constexpr (F32Out) {
+        float* op = static_cast<float*>(out) + ((int64_t)b * Sq + q) * D + h * kD + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        uint2 w;
-        w.x = pack_bf16x2(acc_o[dt][u][0] * inv, acc_o[dt][u][1] * inv);
-        w.y = pack_bf16x2(acc_o[dt][u][2] * inv, acc_o[dt][u][3] * inv);
-        *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<f32x4_t*>(op + 16 * dt) = acc_o[dt][u] * inv;
+      } else {
+        uint16_t* op = static_cast<uint16_t*>(out) + ((int64_t)b * Sq + q) * D + h * kD + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          uint2 w;
+          w.x = pack_bf16x2(acc_o[dt][u][0] * inv, acc_o[dt][u][1] * inv);
+          w.y = pack_bf16x2(acc_o[dt][u][2] * inv, acc_o[dt][u][3] * inv);
+          *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+        }
       }
-      if (lse && grp == 0) lse[(int64_t)bh * S + q] = (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f;
+      if (lse && grp == 0) lse[(int64_t)bh * Sq + q] = (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f;
     }
   }
 }
@@ -267,9 +315,21 @@ hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S,
   const int64_t nblocks = (int64_t)nqt * heads * B;
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), static_cast<uint16_t*>(out), lse, S, heads, nqt,
-                     scale_log2);
+  const auto* src = static_cast<const uint16_t*>(qkv);
+  hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream, src, src,
+                     out, lse, S, S, heads, nqt, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_chunk(const void* q_src, int Sq, const void* kv_src, int Skv, float* out, float* lse, int B,
+                                 int heads, float softmax_scale, hipStream_t stream) {
+  const int nqt = (Sq + kBM - 1) / kBM;
+  const int64_t nblocks = (int64_t)nqt * heads * B;
+  if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), out, lse, Sq, Skv,
+                     heads, nqt, scale_log2);
   return hipGetLastError();
 }
 

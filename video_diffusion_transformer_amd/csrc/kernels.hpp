@@ -17,6 +17,15 @@ hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const f
 hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S, int heads,
                            float softmax_scale, hipStream_t stream);
 
+// Attention of the queries of q_src (Sq rows per batch entry) against the
+// keys/values of kv_src (Skv rows), fp32 output and log-sum-exp.
+hipError_t launch_attn_fwd_chunk(const void* q_src, int Sq, const void* kv_src, int Skv, float* out, float* lse, int B,
+                                 int heads, float softmax_scale, hipStream_t stream);
+
+// In-place log-sum-exp merge of a chunk result into an accumulator.
+hipError_t launch_attn_merge(float* acc, float* acc_lse, const float* chunk, const float* chunk_lse, void* out16,
+                             int B, int Sq, int heads, hipStream_t stream);
+
 // fp8: per-tensor amax + e4m3 quantisation into qk8 [B, S, 2D] and
 // vt8 [B, heads, 128, S_pad] (V transposed per head, zero past S).
 hipError_t launch_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int B, int S,

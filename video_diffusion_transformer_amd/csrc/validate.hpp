@@ -103,6 +103,45 @@ inline int validate_attn(const void* qkv, const void* out, const void* lse, int6
   return WAN_OK;
 }
 
+inline int validate_attn_chunk(const void* q_src, const void* kv_src, const void* out, const void* lse, int64_t B,
+                               int64_t Sq, int64_t Skv, int64_t heads, int64_t head_dim, float scale, Sizes* z) {
+  if (Skv < 0) return WAN_E_SHAPE;
+  if (Skv > kMaxTokens) return WAN_E_OVERFLOW;
+  int rc = check_sizes(B, Sq, heads, head_dim, z);
+  if (rc != WAN_OK) return rc;
+  if (!std::isfinite(scale) || scale <= 0.f) return WAN_E_VALUE;
+  if (z->empty) return WAN_OK;
+  if (Skv == 0) return WAN_E_SHAPE;  // attention over no keys is undefined
+  if (!q_src || !kv_src || !out || !lse) return WAN_E_NULL;
+  if (!aligned(q_src, 16) || !aligned(kv_src, 16) || !aligned(out, 16) || !aligned(lse, 4)) return WAN_E_ALIGN;
+  int64_t kv_elems;
+  if (!mul_ok(B * Skv, 3 * z->D, &kv_elems) || !mul_ok(kv_elems, 2, &kv_elems)) return WAN_E_OVERFLOW;
+  const int64_t q_bytes = z->qkv_elems * 2, out_bytes = z->out_elems * 4, lse_bytes = z->B * z->heads * z->S * 4;
+  if (overlaps(out, out_bytes, q_src, q_bytes) || overlaps(out, out_bytes, kv_src, kv_elems) ||
+      overlaps(lse, lse_bytes, q_src, q_bytes) || overlaps(lse, lse_bytes, kv_src, kv_elems) ||
+      overlaps(lse, lse_bytes, out, out_bytes))
+    return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
+inline int validate_attn_merge(const void* acc, const void* acc_lse, const void* chunk, const void* chunk_lse,
+                               const void* out16, int64_t B, int64_t Sq, int64_t heads, int64_t head_dim, Sizes* z) {
+  int rc = check_sizes(B, Sq, heads, head_dim, z);
+  if (rc != WAN_OK) return rc;
+  if (z->empty) return WAN_OK;
+  if (!acc || !acc_lse || !chunk || !chunk_lse) return WAN_E_NULL;
+  if (!aligned(acc, 16) || !aligned(chunk, 16) || !aligned(acc_lse, 4) || !aligned(chunk_lse, 4) ||
+      (out16 && !aligned(out16, 16)))
+    return WAN_E_ALIGN;
+  const int64_t o_bytes = z->out_elems * 4, l_bytes = z->B * z->heads * z->S * 4, h_bytes = z->out_elems * 2;
+  const void* p[5] = {acc, acc_lse, chunk, chunk_lse, out16};
+  const int64_t n[5] = {o_bytes, l_bytes, o_bytes, l_bytes, h_bytes};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(p[i], n[i], p[j], n[j])) return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 // Bytes of the transposed fp8 V buffer: B * heads * 128 * S_pad, S_pad = S rounded up to 128.
 inline bool fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t* out) {
   const int64_t s_pad = (S + 127) / 128 * 128;

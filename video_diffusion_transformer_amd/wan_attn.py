@@ -6,7 +6,8 @@ live on the GPU; there is no CPU path. If the library is not built the first
 call raises -- nothing falls back to another implementation.
 
 The names follow the C ABI: ``qknorm_rope`` -> wan_qknorm_rope,
-``attn_fwd`` -> wan_attn_fwd, ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
+``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_chunk`` -> wan_attn_fwd_chunk,
+``attn_merge`` -> wan_attn_merge, ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
 ``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
 """
 
@@ -35,6 +36,8 @@ SIGNATURES = {
     "wan_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
+    "wan_attn_fwd_chunk": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _P]),
+    "wan_attn_merge": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qkv_quant_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_fp8_vt_bytes": (ctypes.c_int64, [_I64, _I64, _I64, _I64]),
     "wan_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
@@ -149,6 +152,57 @@ def attn_fwd(qkv, heads, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=Fa
             _ptr(qkv), _ptr(out), _ptr(lse) if want_lse else ctypes.c_void_p(0), B, S, heads,
             head_dim, scale, _stream(qkv.device, stream)))
     return (out, lse) if want_lse else out
+
+
+def attn_fwd_chunk(q_src, kv_src, heads, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=None, stream=None):
+    """Queries of q_src [B, Sq, 3D] against the keys/values of kv_src
+    [B, Skv, 3D] (both packed bf16). Returns (out fp32 [B, Sq, D],
+    lse fp32 [B, heads, Sq])."""
+    _need_gpu("q_src", q_src, torch.bfloat16)
+    _need_gpu("kv_src", kv_src, torch.bfloat16)
+    B, Sq, Skv = q_src.shape[0], q_src.shape[1], kv_src.shape[1]
+    D = heads * head_dim
+    if q_src.dim() != 3 or kv_src.dim() != 3 or q_src.shape[2] != 3 * D or kv_src.shape[2] != 3 * D \
+            or kv_src.shape[0] != B:
+        raise ValueError("q_src and kv_src must be [B, S, 3*heads*head_dim] with the same B")
+    scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else float(softmax_scale)
+    dev = q_src.device
+    out = torch.empty((B, Sq, D), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, heads, Sq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need_gpu("out", out, torch.float32)
+    _need_gpu("lse", lse, torch.float32)
+    if tuple(out.shape) != (B, Sq, D) or tuple(lse.shape) != (B, heads, Sq):
+        raise ValueError("out must be [B, Sq, D] and lse [B, heads, Sq]")
+    with torch.cuda.device(dev):
+        _check("wan_attn_fwd_chunk", lib().wan_attn_fwd_chunk(
+            _ptr(q_src), Sq, _ptr(kv_src), Skv, _ptr(out), _ptr(lse), B, heads, head_dim, scale,
+            _stream(dev, stream)))
+    return out, lse
+
+
+def attn_merge(acc_out, acc_lse, chunk_out, chunk_lse, heads, head_dim=HEAD_DIM, out_bf16=None, stream=None):
+    """Fold (chunk_out, chunk_lse) into (acc_out, acc_lse) in place; optionally
+    also write the merged output as bf16 into out_bf16."""
+    for name, t in (("acc_out", acc_out), ("acc_lse", acc_lse), ("chunk_out", chunk_out), ("chunk_lse", chunk_lse)):
+        _need_gpu(name, t, torch.float32)
+    B, Sq = acc_out.shape[0], acc_out.shape[1]
+    D = heads * head_dim
+    for t in (acc_out, chunk_out):
+        if tuple(t.shape) != (B, Sq, D):
+            raise ValueError("outputs must be [B, Sq, heads*head_dim]")
+    for t in (acc_lse, chunk_lse):
+        if tuple(t.shape) != (B, heads, Sq):
+            raise ValueError("lse tensors must be [B, heads, Sq]")
+    if out_bf16 is not None:
+        _need_gpu("out_bf16", out_bf16, torch.bfloat16)
+        if tuple(out_bf16.shape) != (B, Sq, D):
+            raise ValueError("out_bf16 must be [B, Sq, D]")
+    dev = acc_out.device
+    with torch.cuda.device(dev):
+        _check("wan_attn_merge", lib().wan_attn_merge(
+            _ptr(acc_out), _ptr(acc_lse), _ptr(chunk_out), _ptr(chunk_lse), _ptr(out_bf16), B, Sq, heads,
+            head_dim, _stream(dev, stream)))
+    return acc_out, acc_lse
 
 
 class Fp8QKV:
