@@ -19,8 +19,9 @@
 //     wait + barrier per tile publishes it;
 //   * scores are computed transposed, S^T = K Q^T (16x16x32 MFMA: A = 16 keys x
 //     32 channels from LDS, B = Q held in registers), so after the MFMA each
-//     lane holds scores of ONE query column: the online-softmax max and sum are
-//     lane-local plus two cross-lane steps (lanes l^16, l^32 share the query);
+//     lane holds scores of ONE query column: the online-softmax max is
+//     lane-local, plus two cross-lane steps (lanes l^16, l^32 share the query)
+//     only on the tiles where the running max moves;
 //   * the bf16 probabilities of two adjacent 16-key tiles are already the B
 //     operand of O^T = V^T P^T (lane group g holds keys 4g..4g+3 of each tile);
 //     the V^T A operand is read straight from the row-major V tile with the
@@ -33,8 +34,8 @@
 //     rows one lane group reads, and the 8 V rows x 32 B half a wave reads with
 //     the transposing load, fall in distinct banks;
 //   * the O^T accumulator keeps one query column per lane, so the rescale by
-//     exp2(m_old - m_new) is lane-local, and the row sums of P are accumulated
-//     by one extra MFMA against a row of ones. The running max only moves when a
+//     exp2(m_old - m_new) is lane-local, and each lane sums its own bf16
+//     probabilities (packed dot products with (1, 1)). The running max only moves when a
 //     tile's max exceeds it by more than 8 (log2 units): most tiles skip the
 //     rescale; the stale max keeps p <= 2^8 (exact in fp32, far from bf16
 //     overflow) and the final normalisation uses the same max, so the result is
@@ -64,6 +65,10 @@ constexpr int kBM = 16 * kQT * kWaves;   // query rows per workgroup
 constexpr int kRow = kD * 2;             // bytes per K or V row
 constexpr int kTile = kBN * kRow;        // 16 KB
 constexpr int kStage = 2 * kTile;        // K tile + V tile
+#ifndef WAN_ATTN_SWP
+#define WAN_ATTN_SWP 0
+#endif
+constexpr int kStages = WAN_ATTN_SWP ? 3 : 2;
 constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag behind the true max
 constexpr int kWaitVmem0 = 0x0f70;       // s_waitcnt vmcnt(0), other counters unconstrained
 
@@ -84,58 +89,85 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
 // Per-kernel constants shared by the tile step below.
 struct TileArgs {
   const uint16_t* base;  // K/V rows of this (b, h): element offset of channel 0 of row 0
-  int S, rs, D, nkt, wave, lane, l16, grp, vr;
+  int S, rs, D, nkt, wave, lane, l16, grp;
+  int kb, vb;  // per-lane byte offsets of the first K / V^T fragment read in a stage
+  int gk[16 / kWaves], gv[16 / kWaves];  // per-lane byte offsets of the K / V chunks a lane stages
   float scale_log2;
 };
 
 // Direct global -> LDS staging of one 64-key tile: lane l of a wave
 // instruction lands at the wave-uniform LDS base + 16*l. Each wave fills
-// 16/kWaves 1 KB blocks (4 rows) of the K tile and of the V tile; lane l of a
+// kBlk 1 KB blocks (4 rows) of the K tile and of the V tile; lane l of a
 // block takes physical row 4*blk + l/16, physical chunk l%16, and fetches the
-// logical chunk the swizzle maps there. Rows past the end re-read row S-1
-// (masked later).
-__device__ __forceinline__ void issue_tile(const TileArgs& a, int k0, unsigned char* __restrict__ ks) {
+// logical chunk the swizzle maps there. The per-lane byte offsets from the
+// tile's first row are fixed (gk, gv); only the last tile, whose rows past the
+// end re-read row S-1 (masked later), recomputes them.
+constexpr int kBlk = 16 / kWaves;  // 1 KB blocks per wave per K or V tile
+
+__device__ __forceinline__ int tile_row(const TileArgs& a, int j) { return 4 * (kBlk * a.wave + j) + (a.lane >> 4); }
+
+__device__ __forceinline__ void issue_tile(const TileArgs& a, int k0, unsigned char* __restrict__ smem, int off) {
+  const char* tb = reinterpret_cast<const char*>(a.base + (int64_t)k0 * a.rs);  // wave-uniform
+  unsigned char* dst = smem + off + kBlk * a.wave * 1024;
+  if (k0 + kBN <= a.S) {
 #pragma unroll
-  for (int j = 0; j < 16 / kWaves; ++j) {
-    const int blk = (16 / kWaves) * a.wave + j;
-    const int r = 4 * blk + (a.lane >> 4), pc = a.lane & 15;
-    const uint16_t* rp = a.base + (int64_t)min(k0 + r, a.S - 1) * a.rs;
-    __builtin_amdgcn_global_load_lds(rp + a.D + 8 * (pc ^ k_xor(r)), ks + blk * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(rp + 2 * a.D + 8 * (pc ^ v_xor(r)), ks + kTile + blk * 1024, 16, 0, 0);
+    for (int j = 0; j < kBlk; ++j) {
+      __builtin_amdgcn_global_load_lds(tb + a.gk[j], dst + j * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(tb + a.gv[j], dst + kTile + j * 1024, 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kBlk; ++j) {
+      const int r = tile_row(a, j), pc = a.lane & 15;
+      const int64_t ro = (int64_t)(min(k0 + r, a.S - 1) - k0) * a.rs;
+      __builtin_amdgcn_global_load_lds(tb + 2 * (ro + a.D + 8 * (pc ^ k_xor(r))), dst + j * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(tb + 2 * (ro + 2 * a.D + 8 * (pc ^ v_xor(r))), dst + kTile + j * 1024, 16, 0,
+                                       0);
+    }
   }
 }
 
-// One 64-key tile: scores, online softmax and PV from stage `cur`, while the
-// next tile streams into stage `nxt`.
-__device__ __forceinline__ void tile_step(const TileArgs& a, int kt, const unsigned char* __restrict__ cur,
-                                          unsigned char* __restrict__ nxt, const bf16x8_t (&qf)[kQT][4],
-                                          f32x4_t (&acc_o)[8][kQT], f32x4_t (&acc_l)[kQT], float (&m_run)[kQT],
-                                          const bf16x8_t& ones) {
-  const int k0 = kt * kBN;
-  const unsigned char* ks = cur;
-  const unsigned char* vs = cur + kTile;
-  // The other stage was last read in iteration kt-1, which every wave has left.
-  if (kt + 1 < a.nkt) issue_tile(a, k0 + kBN, nxt);
-
-  // S^T: 4 key tiles (16 keys) x kQT query tiles, K over the 128 channels.
-  f32x4_t acc_s[4][kQT];
+// The tile steps below work on NH 32-key halves of a staged 64-key tile,
+// starting at half h0 (the plain loop takes both halves at once, the pipelined
+// loop one at a time).
+//
+// S^T: 16-key tiles t = 2h0 .. 2h0+2NH-1 x kQT query tiles, K over the 128
+// channels. A = 16 keys x 32 channels from LDS, B = Q in registers. Lane
+// (l16, grp) reads row 16t + l16, logical chunk 4k + grp, at physical chunk
+// (4k + grp) ^ l16: byte offset kb ^ 64k (kb = the k = 0 offset) plus 4096t.
+// The stage offset (a multiple of 16 KB) is added before the XOR and hidden
+// from the optimiser, so the four addresses cost one XOR each per step instead
+// of four registers held across the loop.
+template <int NH>
+__device__ __forceinline__ void tile_scores(const TileArgs& a, const unsigned char* __restrict__ smem, int k_off,
+                                            int h0, const bf16x8_t (&qf)[kQT][4], f32x4_t (&acc_s)[2 * NH][kQT]) {
+  int x = k_off + a.kb + 8192 * h0;
+  asm("" : "+v"(x));
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 2 * NH; ++t) {
 #pragma unroll
     for (int u = 0; u < kQT; ++u) acc_s[t][u] = f32x4_t{};
-    const int r = 16 * t + a.l16;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ks + r * kRow + 16 * ((4 * k + a.grp) ^ k_xor(r)));
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(smem + (x ^ (64 * k)) + 4096 * t);
 #pragma unroll
       for (int u = 0; u < kQT; ++u) acc_s[t][u] = mfma16(av, qf[u][k], acc_s[t][u]);
     }
   }
+}
 
+// Max step of the online softmax (base-2, scale folded in) over the keys
+// k0 .. k0 + 32NH - 1: masks keys past the end, and moves the running max of a
+// query column only when these keys' max exceeds it by more than the slack.
+// The row sums are rescaled here; returns a bit per query tile whose max
+// moved, with the factor alpha the output accumulator must be scaled by.
+template <int NH>
+__device__ __forceinline__ unsigned tile_max(const TileArgs& a, int k0, f32x4_t (&acc_s)[2 * NH][kQT],
+                                             float (&m_run)[kQT], float (&acc_l)[kQT], float (&alpha)[kQT]) {
   // Mask keys past the end (only the last tile can have them).
-  if (k0 + kBN > a.S) {
+  if (k0 + 32 * NH > a.S) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2 * NH; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (k0 + 16 * t + 4 * a.grp + i >= a.S) {
@@ -143,60 +175,93 @@ __device__ __forceinline__ void tile_step(const TileArgs& a, int kt, const unsig
           for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
         }
   }
-
-  // Online softmax per query column (base-2, scale folded in), lazily rescaled.
-  bf16x8_t pf[kQT][2];
+  unsigned moved = 0;
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
     float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
 #pragma unroll
-    for (int t = 1; t < 4; ++t)
+    for (int t = 1; t < 2 * NH; ++t)
       mx = fmaxf(mx, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+    // The four lanes of a query column share m_run, so one of them exceeding
+    // m_run + slack with its own scores is the same test as the column max
+    // doing so: the cross-lane reduction is only needed when the max moves.
+    mx *= a.scale_log2;
+    alpha[u] = 1.0f;
     if (__ballot(mx > m_run[u] + kRescaleSlack)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run[u], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
+      alpha[u] = __builtin_amdgcn_exp2f(m_run[u] - m_new);
       m_run[u] = m_new;
+      acc_l[u] *= alpha[u];
+      moved |= 1u << u;
+    }
+  }
+  return moved;
+}
+
+// Scales the output accumulator of the query tiles whose max moved.
+__device__ __forceinline__ void tile_rescale(unsigned moved, const float (&alpha)[kQT], f32x4_t (&acc_o)[8][kQT]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc_l[u][i] *= alpha;
+  for (int u = 0; u < kQT; ++u)
+    if (moved & (1u << u)) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
+        for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha[u];
     }
+}
+
+// p = 2^(s * scale_log2 - m) rounded to bf16, written in the B-operand layout
+// of PV (one 32-key step per half: lane group g holds keys 4g..4g+3 of both
+// 16-key tiles). The row sums add up exactly these bf16 weights (a dot product
+// of each packed pair with (1, 1), fp32 sum), so the normalisation matches
+// what PV accumulated; each lane sums its own keys.
+template <int NH>
+__device__ __forceinline__ void tile_exp(const TileArgs& a, const f32x4_t (&acc_s)[2 * NH][kQT],
+                                         const float (&m_run)[kQT], bf16x8_t (&pf)[kQT][NH], float (&acc_l)[kQT]) {
+  const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+  for (int u = 0; u < kQT; ++u)
+#pragma unroll
+    for (int c = 0; c < NH; ++c) {
       bf16x8_t v;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], a.scale_log2, -m_run[u]));
       pf[u][c] = v;
-      acc_l[u] = mfma16(ones, v, acc_l[u]);
+      // Literal shuffles: extracting the pairs through a bit cast to 32-bit
+      // lanes is miscompiled for this builtin (every call read the first pair).
+      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc_l[u], false);
+      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, acc_l[u], false);
+      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, acc_l[u], false);
+      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, acc_l[u], false);
     }
-  }
+}
 
-  // Let the next tile's direct-to-LDS writes finish before the transposed V
-  // reads: measured, the PV phase runs faster without those writes competing
-  // for the LDS, and the loads have had the score and softmax phases to land.
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-  // O^T (channels x queries) += V^T P^T: 8 channel tiles x 2 key steps of 32.
+// O^T (channels x queries) += V^T P^T over halves h0 .. h0+NH-1: 8 channel
+// tiles x one 32-key step per half. The V^T fragment comes from two
+// transposing LDS reads of the row-major V tile: lane (l16, grp) reads rows
+// 32h + 4grp + l16/4 (+16), logical chunk 2dt + (l16%4)/2, half l16%2. The
+// swizzle XORs the chunk with 2 (row % 8), so the byte offset is vb ^ 32dt
+// (vb = the dt = 0 offset) plus 8192h (+4096); as for K, one XOR per address.
+template <int NH>
+__device__ __forceinline__ void tile_pv(const TileArgs& a, const unsigned char* __restrict__ smem, int v_off, int h0,
+                                        const bf16x8_t (&pf)[kQT][NH], f32x4_t (&acc_o)[8][kQT]) {
+  int x = v_off + a.vb + 8192 * h0;
+  asm("" : "+v"(x));
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const int ch = 2 * dt + ((a.l16 & 3) >> 1), sub = 8 * (a.l16 & 1);
+    const unsigned char* p = smem + (x ^ (32 * dt));
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int r0 = 32 * c + a.vr, r1 = r0 + 16;
-      const s16x4_t lo = lds_read_tr16(vs + r0 * kRow + 16 * (ch ^ v_xor(r0)) + sub);
-      const s16x4_t hi4 = lds_read_tr16(vs + r1 * kRow + 16 * (ch ^ v_xor(r1)) + sub);
+    for (int c = 0; c < NH; ++c) {
+      const s16x4_t lo = lds_read_tr16(p + 8192 * c);
+      const s16x4_t hi4 = lds_read_tr16(p + 8192 * c + 4096);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int u = 0; u < kQT; ++u) acc_o[dt][u] = mfma16(av, pf[u][c], acc_o[dt][u]);
     }
   }
-
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
-  __syncthreads();                          // ... and every wave's; stage `cur` is free again
 }
 
 // Queries come from the Q part of one packed buffer (Sq rows per batch entry),
@@ -207,7 +272,7 @@ template <bool F32Out>
 __global__ void __launch_bounds__(kThreads, (kQT >= 4 || kWaves > 4) ? 1 : 2)
 attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ kvsrc, void* __restrict__ out,
                 float* __restrict__ lse, int Sq, int S, int heads, int nqt, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStage];
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = lid % nqt;
@@ -224,11 +289,21 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
   a.rs = rs;
   a.D = D;
   a.nkt = (S + kBN - 1) / kBN;
-  a.wave = wave;
+  a.wave = __builtin_amdgcn_readfirstlane(wave);
   a.lane = lane;
   a.l16 = l16;
   a.grp = grp;
-  a.vr = 4 * grp + (l16 >> 2);  // V^T source row 4*grp + l16/4 (+32c, +16)
+#pragma unroll
+  for (int j = 0; j < kBlk; ++j) {
+    const int r = tile_row(a, j), pc = lane & 15;
+    a.gk[j] = 2 * (r * rs + D + 8 * (pc ^ k_xor(r)));
+    a.gv[j] = 2 * (r * rs + 2 * D + 8 * (pc ^ v_xor(r)));
+  }
+  a.kb = l16 * kRow + 16 * ((grp ^ l16) & 3) + 64 * (l16 >> 2);
+  {
+    const int vr = 4 * grp + (l16 >> 2);  // V^T source row (+32c, +16)
+    a.vb = kTile + vr * kRow + 32 * (vr & 7) + 16 * ((l16 & 3) >> 1) + 8 * (l16 & 1);
+  }
   a.scale_log2 = scale_log2;
 
   // Q fragments (B operand of S^T = K Q^T): query 16u + l16 of this wave,
@@ -253,37 +328,87 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
 #pragma unroll
     for (int k = 0; k < 4; ++k) asm volatile("" ::"v"(qf[u][k]));
 
-  // Row sums of P come from the MFMA too: an A operand whose row 0 is all
-  // bf16 ones (rows 1..15 zero) times P^T gives, in register 0 of lane l16 of
-  // lane group 0, the sum of the bf16 probabilities of query l16 -- one extra
-  // MFMA per 32 keys instead of a VALU add per score, and the normalisation uses
-  // exactly the weights PV used.
-  f32x4_t acc_o[8][kQT], acc_l[kQT];
-  float m_run[kQT];
-  const unsigned short one = l16 == 0 ? 0x3f80 : 0;
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, s16x8_t{(short)one, (short)one, (short)one, (short)one,
-                                                              (short)one, (short)one, (short)one, (short)one});
+  f32x4_t acc_o[8][kQT];
+  float acc_l[kQT], m_run[kQT];  // per-lane partial row sums (this lane's keys), running max
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc_o[i][u] = f32x4_t{};
-    acc_l[u] = f32x4_t{};
+    acc_l[u] = 0.0f;
     m_run[u] = -INFINITY;
   }
 
-  issue_tile(a, 0, smem);
+  float alpha[kQT];
+  issue_tile(a, 0, smem, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
-  for (int kt = 0; kt < a.nkt; ++kt) {
-    unsigned char* cur = smem + (kt & 1) * kStage;
-    unsigned char* nxt = smem + ((kt + 1) & 1) * kStage;
-    tile_step(a, kt, cur, nxt, qf, acc_o, acc_l, m_run, ones);
+#if WAN_ATTN_SWP
+  // Software pipeline over 32-key halves and three LDS stages: each step
+  // computes the scores and probabilities of one half while the PV product of
+  // the previous half runs, so the exponentials overlap MFMAs. The
+  // accumulators see the same operations in the same order as the plain loop:
+  // O^T is scaled by a half's factor after the previous half's PV is added
+  // and before its own is.
+  f32x4_t acc_s[2][kQT];
+  bf16x8_t pf[kQT][1], pn[kQT][1];
+  unsigned moved = 0;  // query tiles whose max moved at the previous half
+  auto step = [&](int k_off, int h, int key0, int v_off, int vh, bool pv) {
+    if (moved) tile_rescale(moved, alpha, acc_o);
+    tile_scores<1>(a, smem, k_off, h, qf, acc_s);
+    moved = tile_max<1>(a, key0, acc_s, m_run, acc_l, alpha);
+    // One straight-line block: the exponentials of this half and the PV
+    // MFMAs of the previous half are independent and interleave.
+    tile_exp<1>(a, acc_s, m_run, pn, acc_l);
+    if (pv) tile_pv<1>(a, smem, v_off, vh, pf, acc_o);
+#pragma unroll
+    for (int u = 0; u < kQT; ++u) pf[u][0] = pn[u][0];
+  };
+  // Tile 0: its first half has no predecessor.
+  if (a.nkt > 1) issue_tile(a, kBN, smem, kStage);
+  step(0, 0, 0, 0, 0, false);
+  step(0, 1, 32, 0, 0, true);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  __syncthreads();
+  int sc = 1;  // stage of tile kt
+  for (int kt = 1; kt < a.nkt; ++kt) {
+    const int sn = sc == kStages - 1 ? 0 : sc + 1;  // stage of tile kt+1 (held tile kt-2, last read in kt-1)
+    const int sp = sc == 0 ? kStages - 1 : sc - 1;  // stage of tile kt-1
+    if (kt + 1 < a.nkt) issue_tile(a, kt * kBN + kBN, smem, sn * kStage);
+    step(sc * kStage, 0, kt * kBN, sp * kStage, 1, true);
+    step(sc * kStage, 1, kt * kBN + 32, sc * kStage, 0, true);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
+    __syncthreads();                          // ... and every wave's; tile kt-1's stage is free
+    sc = sn;
   }
+  if (moved) tile_rescale(moved, alpha, acc_o);
+  tile_pv<1>(a, smem, ((a.nkt - 1) % kStages) * kStage, 1, pf, acc_o);
+#else
+  f32x4_t acc_s[4][kQT];
+  bf16x8_t pf[kQT][2];
+  for (int kt = 0; kt < a.nkt; ++kt) {
+    const int cur = (kt & 1) * kStage;
+    // The other stage was last read in iteration kt-1, which every wave has left.
+    if (kt + 1 < a.nkt) issue_tile(a, kt * kBN + kBN, smem, ((kt + 1) & 1) * kStage);
+    tile_scores<2>(a, smem, cur, 0, qf, acc_s);
+    const unsigned moved = tile_max<2>(a, kt * kBN, acc_s, m_run, acc_l, alpha);
+    if (moved) tile_rescale(moved, alpha, acc_o);
+    tile_exp<2>(a, acc_s, m_run, pf, acc_l);
+    // Let the next tile's direct-to-LDS writes finish before the transposed V
+    // reads: measured, the PV phase runs faster without those writes competing
+    // for the LDS, and the loads have had the score and softmax phases to land.
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    tile_pv<2>(a, smem, cur, 0, pf, acc_o);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
+    __syncthreads();                          // ... and every wave's; this stage is free again
+  }
+#endif
 
   // Epilogue: O = O^T / l; lane holds 4 consecutive channels per (dt, u).
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
-    const float l_tot = __shfl(acc_l[u][0], l16, 64);  // sum of the bf16 P of query l16, in lane l16
+    float l_tot = acc_l[u];  // the four lanes of a query column hold disjoint keys
+    l_tot += __shfl_xor(l_tot, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
     const int q = q0 + 16 * u + l16;
     if (q < Sq) {
       const float inv = 1.0f / l_tot;

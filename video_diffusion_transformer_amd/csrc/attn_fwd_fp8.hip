@@ -174,9 +174,13 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int i = (t == 0 ? 2 : 0); i < 4; i += 2) mx = fmaxf(mx, fmaxf(acc_s[t][u][i], acc_s[t][u][i + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c_log2;
+      // Lanes l, l^16, l^32, l^48 share the query and its m_run: testing each
+      // lane's own max is the same as testing the column max, so the
+      // cross-lane reduction runs only when the max moves.
+      mx *= c_log2;
       if (__ballot(mx > m_run[u] + kRescaleSlack)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run[u], mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
         m_run[u] = m_new;
