@@ -65,10 +65,7 @@ constexpr int kBM = 16 * kQT * kWaves;   // query rows per workgroup
 constexpr int kRow = kD * 2;             // bytes per K or V row
 constexpr int kTile = kBN * kRow;        // 16 KB
 constexpr int kStage = 2 * kTile;        // K tile + V tile
-#ifndef WAN_ATTN_SWP
-#define WAN_ATTN_SWP 0
-#endif
-constexpr int kStages = WAN_ATTN_SWP ? 3 : 2;
+constexpr int kStages = 2;               // LDS stages (K + V tile each)
 constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag behind the true max
 constexpr int kWaitVmem0 = 0x0f70;       // s_waitcnt vmcnt(0), other counters unconstrained
 
@@ -91,7 +88,7 @@ struct TileArgs {
   const uint16_t* base;  // K/V rows of this (b, h): element offset of channel 0 of row 0
   int S, rs, D, nkt, wave, lane, l16, grp;
   int kb, vb;  // per-lane byte offsets of the first K / V^T fragment read in a stage
-  int gk[16 / kWaves], gv[16 / kWaves];  // per-lane byte offsets of the K / V chunks a lane stages
+  uint32_t gk[16 / kWaves], gv[16 / kWaves];  // per-lane byte offsets of the K / V chunks a lane stages
   float scale_log2;
 };
 
@@ -127,24 +124,19 @@ __device__ __forceinline__ void issue_tile(const TileArgs& a, int k0, unsigned c
   }
 }
 
-// The tile steps below work on NH 32-key halves of a staged 64-key tile,
-// starting at half h0 (the plain loop takes both halves at once, the pipelined
-// loop one at a time).
-//
-// S^T: 16-key tiles t = 2h0 .. 2h0+2NH-1 x kQT query tiles, K over the 128
-// channels. A = 16 keys x 32 channels from LDS, B = Q in registers. Lane
-// (l16, grp) reads row 16t + l16, logical chunk 4k + grp, at physical chunk
-// (4k + grp) ^ l16: byte offset kb ^ 64k (kb = the k = 0 offset) plus 4096t.
-// The stage offset (a multiple of 16 KB) is added before the XOR and hidden
-// from the optimiser, so the four addresses cost one XOR each per step instead
-// of four registers held across the loop.
-template <int NH>
+// S^T for one 64-key tile: 4 key tiles (16 keys) x kQT query tiles, K over
+// the 128 channels. A = 16 keys x 32 channels from LDS, B = Q in registers.
+// Lane (l16, grp) reads row 16t + l16, logical chunk 4k + grp, at physical
+// chunk (4k + grp) ^ l16: byte offset kb ^ 64k (kb = the k = 0 offset) plus
+// 4096t. The stage offset (a multiple of 32 KB) is added before the XOR and
+// hidden from the optimiser, so the four addresses cost one XOR each per tile
+// instead of four registers held across the loop.
 __device__ __forceinline__ void tile_scores(const TileArgs& a, const unsigned char* __restrict__ smem, int k_off,
-                                            int h0, const bf16x8_t (&qf)[kQT][4], f32x4_t (&acc_s)[2 * NH][kQT]) {
-  int x = k_off + a.kb + 8192 * h0;
+                                            const bf16x8_t (&qf)[kQT][4], f32x4_t (&acc_s)[4][kQT]) {
+  int x = k_off + a.kb;
   asm("" : "+v"(x));
 #pragma unroll
-  for (int t = 0; t < 2 * NH; ++t) {
+  for (int t = 0; t < 4; ++t) {
 #pragma unroll
     for (int u = 0; u < kQT; ++u) acc_s[t][u] = f32x4_t{};
 #pragma unroll
@@ -156,18 +148,17 @@ __device__ __forceinline__ void tile_scores(const TileArgs& a, const unsigned ch
   }
 }
 
-// Max step of the online softmax (base-2, scale folded in) over the keys
-// k0 .. k0 + 32NH - 1: masks keys past the end, and moves the running max of a
-// query column only when these keys' max exceeds it by more than the slack.
-// The row sums are rescaled here; returns a bit per query tile whose max
-// moved, with the factor alpha the output accumulator must be scaled by.
-template <int NH>
-__device__ __forceinline__ unsigned tile_max(const TileArgs& a, int k0, f32x4_t (&acc_s)[2 * NH][kQT],
+// Max step of the online softmax of one tile (base-2, scale folded in): masks
+// keys past the end, and moves the running max of a query column only when the
+// tile's max exceeds it by more than the slack. The row sums are rescaled here;
+// returns a bit per query tile whose max moved, with the factor alpha the
+// output accumulator must be scaled by.
+__device__ __forceinline__ unsigned tile_max(const TileArgs& a, int k0, f32x4_t (&acc_s)[4][kQT],
                                              float (&m_run)[kQT], float (&acc_l)[kQT], float (&alpha)[kQT]) {
   // Mask keys past the end (only the last tile can have them).
-  if (k0 + 32 * NH > a.S) {
+  if (k0 + kBN > a.S) {
 #pragma unroll
-    for (int t = 0; t < 2 * NH; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (k0 + 16 * t + 4 * a.grp + i >= a.S) {
@@ -180,10 +171,10 @@ __device__ __forceinline__ unsigned tile_max(const TileArgs& a, int k0, f32x4_t 
   for (int u = 0; u < kQT; ++u) {
     float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
 #pragma unroll
-    for (int t = 1; t < 2 * NH; ++t)
+    for (int t = 1; t < 4; ++t)
       mx = fmaxf(mx, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
     // The four lanes of a query column share m_run, so one of them exceeding
-    // m_run + slack with its own scores is the same test as the column max
+    // m_run + slack with its own 16 scores is the same test as the column max
     // doing so: the cross-lane reduction is only needed when the max moves.
     mx *= a.scale_log2;
     alpha[u] = 1.0f;
@@ -213,25 +204,24 @@ __device__ __forceinline__ void tile_rescale(unsigned moved, const float (&alpha
 }
 
 // p = 2^(s * scale_log2 - m) rounded to bf16, written in the B-operand layout
-// of PV (one 32-key step per half: lane group g holds keys 4g..4g+3 of both
-// 16-key tiles). The row sums add up exactly these bf16 weights (a dot product
-// of each packed pair with (1, 1), fp32 sum), so the normalisation matches
-// what PV accumulated; each lane sums its own keys.
-template <int NH>
-__device__ __forceinline__ void tile_exp(const TileArgs& a, const f32x4_t (&acc_s)[2 * NH][kQT],
-                                         const float (&m_run)[kQT], bf16x8_t (&pf)[kQT][NH], float (&acc_l)[kQT]) {
+// of PV (two 32-key steps per query tile: lane group g holds keys 4g..4g+3 of
+// 16-key tiles 2c and 2c+1). The row sums add up exactly these bf16 weights (a
+// dot product of each packed pair with (1, 1), fp32 sum), so the
+// normalisation matches what PV accumulated; each lane sums its own keys.
+__device__ __forceinline__ void tile_exp(const TileArgs& a, const f32x4_t (&acc_s)[4][kQT], const float (&m_run)[kQT],
+                                         bf16x8_t (&pf)[kQT][2], float (&acc_l)[kQT]) {
   const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
   for (int u = 0; u < kQT; ++u)
 #pragma unroll
-    for (int c = 0; c < NH; ++c) {
+    for (int c = 0; c < 2; ++c) {
       bf16x8_t v;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], a.scale_log2, -m_run[u]));
       pf[u][c] = v;
       // Literal shuffles: extracting the pairs through a bit cast to 32-bit
-      // lanes is miscompiled for this builtin (every call read the first pair).
+      // lanes is miscompiled by this clang (every extraction read element 0).
       acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc_l[u], false);
       acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, acc_l[u], false);
       acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, acc_l[u], false);
@@ -239,22 +229,21 @@ __device__ __forceinline__ void tile_exp(const TileArgs& a, const f32x4_t (&acc_
     }
 }
 
-// O^T (channels x queries) += V^T P^T over halves h0 .. h0+NH-1: 8 channel
-// tiles x one 32-key step per half. The V^T fragment comes from two
-// transposing LDS reads of the row-major V tile: lane (l16, grp) reads rows
-// 32h + 4grp + l16/4 (+16), logical chunk 2dt + (l16%4)/2, half l16%2. The
-// swizzle XORs the chunk with 2 (row % 8), so the byte offset is vb ^ 32dt
-// (vb = the dt = 0 offset) plus 8192h (+4096); as for K, one XOR per address.
-template <int NH>
-__device__ __forceinline__ void tile_pv(const TileArgs& a, const unsigned char* __restrict__ smem, int v_off, int h0,
-                                        const bf16x8_t (&pf)[kQT][NH], f32x4_t (&acc_o)[8][kQT]) {
-  int x = v_off + a.vb + 8192 * h0;
+// O^T (channels x queries) += V^T P^T over one tile: 8 channel tiles x 2 key
+// steps of 32. The V^T fragment comes from two transposing LDS reads of the
+// row-major V tile: lane (l16, grp) reads rows 32c + 4grp + l16/4 (+16),
+// logical chunk 2dt + (l16%4)/2, half l16%2. The swizzle XORs the chunk with
+// 2 (row % 8), so the byte offset is vb ^ 32dt (vb = the dt = 0 offset) plus
+// 8192c (+4096); as for K, one XOR per address.
+__device__ __forceinline__ void tile_pv(const TileArgs& a, const unsigned char* __restrict__ smem, int v_off,
+                                        const bf16x8_t (&pf)[kQT][2], f32x4_t (&acc_o)[8][kQT]) {
+  int x = v_off + a.vb;
   asm("" : "+v"(x));
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     const unsigned char* p = smem + (x ^ (32 * dt));
 #pragma unroll
-    for (int c = 0; c < NH; ++c) {
+    for (int c = 0; c < 2; ++c) {
       const s16x4_t lo = lds_read_tr16(p + 8192 * c);
       const s16x4_t hi4 = lds_read_tr16(p + 8192 * c + 4096);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -339,69 +328,27 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
   }
 
   float alpha[kQT];
+  f32x4_t acc_s[4][kQT];
+  bf16x8_t pf[kQT][2];
   issue_tile(a, 0, smem, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
-#if WAN_ATTN_SWP
-  // Software pipeline over 32-key halves and three LDS stages: each step
-  // computes the scores and probabilities of one half while the PV product of
-  // the previous half runs, so the exponentials overlap MFMAs. The
-  // accumulators see the same operations in the same order as the plain loop:
-  // O^T is scaled by a half's factor after the previous half's PV is added
-  // and before its own is.
-  f32x4_t acc_s[2][kQT];
-  bf16x8_t pf[kQT][1], pn[kQT][1];
-  unsigned moved = 0;  // query tiles whose max moved at the previous half
-  auto step = [&](int k_off, int h, int key0, int v_off, int vh, bool pv) {
-    if (moved) tile_rescale(moved, alpha, acc_o);
-    tile_scores<1>(a, smem, k_off, h, qf, acc_s);
-    moved = tile_max<1>(a, key0, acc_s, m_run, acc_l, alpha);
-    // One straight-line block: the exponentials of this half and the PV
-    // MFMAs of the previous half are independent and interleave.
-    tile_exp<1>(a, acc_s, m_run, pn, acc_l);
-    if (pv) tile_pv<1>(a, smem, v_off, vh, pf, acc_o);
-#pragma unroll
-    for (int u = 0; u < kQT; ++u) pf[u][0] = pn[u][0];
-  };
-  // Tile 0: its first half has no predecessor.
-  if (a.nkt > 1) issue_tile(a, kBN, smem, kStage);
-  step(0, 0, 0, 0, 0, false);
-  step(0, 1, 32, 0, 0, true);
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-  __syncthreads();
-  int sc = 1;  // stage of tile kt
-  for (int kt = 1; kt < a.nkt; ++kt) {
-    const int sn = sc == kStages - 1 ? 0 : sc + 1;  // stage of tile kt+1 (held tile kt-2, last read in kt-1)
-    const int sp = sc == 0 ? kStages - 1 : sc - 1;  // stage of tile kt-1
-    if (kt + 1 < a.nkt) issue_tile(a, kt * kBN + kBN, smem, sn * kStage);
-    step(sc * kStage, 0, kt * kBN, sp * kStage, 1, true);
-    step(sc * kStage, 1, kt * kBN + 32, sc * kStage, 0, true);
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
-    __syncthreads();                          // ... and every wave's; tile kt-1's stage is free
-    sc = sn;
-  }
-  if (moved) tile_rescale(moved, alpha, acc_o);
-  tile_pv<1>(a, smem, ((a.nkt - 1) % kStages) * kStage, 1, pf, acc_o);
-#else
-  f32x4_t acc_s[4][kQT];
-  bf16x8_t pf[kQT][2];
   for (int kt = 0; kt < a.nkt; ++kt) {
     const int cur = (kt & 1) * kStage;
     // The other stage was last read in iteration kt-1, which every wave has left.
     if (kt + 1 < a.nkt) issue_tile(a, kt * kBN + kBN, smem, ((kt + 1) & 1) * kStage);
-    tile_scores<2>(a, smem, cur, 0, qf, acc_s);
-    const unsigned moved = tile_max<2>(a, kt * kBN, acc_s, m_run, acc_l, alpha);
+    tile_scores(a, smem, cur, qf, acc_s);
+    const unsigned moved = tile_max(a, kt * kBN, acc_s, m_run, acc_l, alpha);
     if (moved) tile_rescale(moved, alpha, acc_o);
-    tile_exp<2>(a, acc_s, m_run, pf, acc_l);
+    tile_exp(a, acc_s, m_run, pf, acc_l);
     // Let the next tile's direct-to-LDS writes finish before the transposed V
     // reads: measured, the PV phase runs faster without those writes competing
     // for the LDS, and the loads have had the score and softmax phases to land.
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    tile_pv<2>(a, smem, cur, 0, pf, acc_o);
+    tile_pv(a, smem, cur, pf, acc_o);
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
     __syncthreads();                          // ... and every wave's; this stage is free again
   }
-#endif
 
   // Epilogue: O = O^T / l; lane holds 4 consecutive channels per (dt, u).
 #pragma unroll

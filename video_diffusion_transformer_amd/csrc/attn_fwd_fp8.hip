@@ -42,7 +42,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kBN = 128;                 // keys per unit
 #ifndef WAN_FP8_WAVES
-#define WAN_FP8_WAVES 4
+#define WAN_FP8_WAVES 8
 #endif
 constexpr int kWaves = WAN_FP8_WAVES;
 constexpr int kThreads = 64 * kWaves;
