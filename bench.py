@@ -18,6 +18,10 @@ line is printed.
               summary when it was taken on the current kernel source, else null.
   cpu_baseline the fp64 numpy oracle on the host cores, on a bounded sample of
               the same workload (query rows of one head against all keys).
+  ring_share  (bf16 workloads) one GPU's share of ring attention with the
+              sequence split over --ring-cp ranks: S/cp queries against cp
+              K/V chunks, each followed by the log-sum-exp merge; not part of
+              the step or of value.
 """
 
 import argparse
@@ -83,6 +87,57 @@ def cpu_baseline(w, budget_s=12.0):
                       f"{w.attn_flop() / (flop / dt):.0f} s"}
 
 
+def ring_share(w, qkv, cp, reps=3):
+    """One GPU's share of a ring-attention call with the sequence split over cp
+    ranks: its S/cp queries attend each of the cp K/V chunks (wan_attn_fwd_chunk)
+    and the partial results are folded by the log-sum-exp merge (wan_attn_merge).
+    Times reps whole shares after one warm-up, with HIP events on the stream."""
+    import torch
+
+    from video_diffusion_transformer_amd import wan_attn
+
+    if cp < 2 or w.S % cp or w.dtype != "bf16":
+        return None
+    sq = w.S // cp
+    dev = qkv.device
+    shard = qkv[:, :sq].contiguous()
+    chunks = [qkv[:, c * sq:(c + 1) * sq].contiguous() for c in range(cp)]
+    o = torch.empty((w.B, sq, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.heads, sq), dtype=torch.float32, device=dev)
+    acc = torch.empty_like(o)
+    acc_lse = torch.empty_like(lse)
+    out16 = torch.empty((w.B, sq, w.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def share(ev=None):
+        acc_lse.fill_(-math.inf)  # empty accumulator
+        for c in range(cp):
+            wan_attn.attn_fwd_chunk(shard, chunks[c], w.heads, out=o, lse=lse)
+            if ev: ev[c][0].record(stream)
+            wan_attn.attn_merge(acc, acc_lse, o, lse, w.heads, out_bf16=out16 if c == cp - 1 else None)
+            if ev: ev[c][1].record(stream)
+
+    share()
+    torch.cuda.synchronize()
+    evs = [[[E(), E()] for _ in range(cp)] for _ in range(reps)]
+    t0, t1 = E(), E()
+    t0.record(stream)
+    for r in range(reps):
+        share(evs[r])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    merge_ms = sum(e[0].elapsed_time(e[1]) for ev in evs for e in ev) / (reps * cp)
+    flop = 4.0 * w.B * w.heads * sq * w.S * 128
+    merge_bytes = w.B * sq * w.D * 4 * 3 + w.B * w.heads * sq * 4 * 3  # read acc + chunk, write acc; LSEs
+    return {"cp": cp, "queries": sq, "ms_per_share": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "merge_ms_per_call": round(merge_ms, 4),
+            "merge_gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
+            "note": "attention of S/cp local queries against cp K/V chunks of S/cp keys + cp merges; "
+                    "TFLOP/s counts the attention FLOP of the share over the whole share time"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +145,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "720p_fp8", "long", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring-cp", type=int, default=8, metavar="CP",
+                    help="also time one GPU's share of ring attention with the sequence split over CP ranks "
+                         "(bf16 workloads; 0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, run one plain device copy of MIB MiB (its hardware "
                          "counters scale FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -186,6 +244,10 @@ def main():
     }
     if fp8:
         rec["quant_ms_per_launch"] = round(quant_ms, 4)
+    if args.ring_cp:
+        ring = ring_share(w, qkv, args.ring_cp)
+        if ring:
+            rec["ring_share"] = ring
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -91,6 +91,22 @@ def test_chunk_matches_oracle_chunk_and_full_kernel():
     assert torch.equal(full_f32.to(torch.bfloat16), full_bf16)
 
 
+def test_merge_into_empty_accumulator_ignores_its_contents():
+    """An accumulator row with LSE = -inf is empty: the merge returns the chunk
+    exactly, whatever the accumulator's output rows hold (here NaN)."""
+    B, Sq, heads = 1, 70, 2
+    D = heads * 128
+    qkv = synth.make_qkv(B, Sq, heads, seed=33).to(DEV)
+    o, l = wan_attn.attn_fwd_chunk(qkv, qkv, heads)
+    acc = torch.full((B, Sq, D), math.nan, dtype=torch.float32, device=DEV)
+    acc_lse = torch.full((B, heads, Sq), -math.inf, dtype=torch.float32, device=DEV)
+    out16 = torch.empty((B, Sq, D), dtype=torch.bfloat16, device=DEV)
+    wan_attn.attn_merge(acc, acc_lse, o, l, heads, out_bf16=out16)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, o) and torch.equal(acc_lse, l)
+    assert torch.equal(out16, o.to(torch.bfloat16))
+
+
 def test_chunk_errors():
     q = torch.zeros((1, 8, 768), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(wan_attn.WanError) as e:

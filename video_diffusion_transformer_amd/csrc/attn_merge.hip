@@ -32,7 +32,9 @@ attn_merge_kernel(float* __restrict__ acc, float* __restrict__ acc_lse, const fl
   const float wa = la == -INFINITY ? 0.f : expf(la - L);
   const float wc = lc == -INFINITY ? 0.f : expf(lc - L);
   const int64_t off = row * (int64_t)heads * 128 + h * 128 + 2 * lane;
-  const float2 a = *reinterpret_cast<const float2*>(acc + off);
+  // An empty accumulator row is not read: whatever it holds (e.g. a fresh
+  // allocation) must not leak into the result through 0 * NaN.
+  const float2 a = la == -INFINITY ? make_float2(0.f, 0.f) : *reinterpret_cast<const float2*>(acc + off);
   const float2 c = *reinterpret_cast<const float2*>(co + off);
   const float2 r = make_float2(wa * a.x + wc * c.x, wa * a.y + wc * c.y);
   *reinterpret_cast<float2*>(acc + off) = r;
