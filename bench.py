@@ -5,7 +5,8 @@
 A step is the whole hot path over one batch of synthetic input already resident
 in HBM: in-place Q/K RMSNorm + bf16 rounding + 3-D RoPE on the packed [Q|K|V]
 buffer, then bidirectional attention over every token (the fp8 workload adds
-the per-tensor e4m3 quantisation and runs attention on fp8 MFMA). W untimed
+the per-tensor e4m3 quantisation, its amax taken in the norm pass, and runs
+attention on fp8 MFMA). W untimed
 warm-up steps, then K timed steps between device synchronisations. One JSON
 line is printed.
 
@@ -145,6 +146,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "720p_fp8", "long", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-unfused", action="store_true",
+                    help="fp8 workload: run norm + RoPE and the quantisation as two calls (separate amax pass) "
+                         "instead of wan_qknorm_rope_quant_fp8")
     ap.add_argument("--ring-cp", type=int, default=8, metavar="CP",
                     help="also time one GPU's share of ring attention with the sequence split over CP ranks "
                          "(bf16 workloads; 0 to skip)")
@@ -177,14 +181,19 @@ def main():
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        wan_attn.qknorm_rope(qkv, gq, gk, grid, w.heads)
-        if ev: ev[1].record(stream)
-        if fp8:
-            wan_attn.qkv_quant_fp8(qkv, w.heads, out=f8)
+        if fp8 and not args.fp8_unfused:
+            wan_attn.qknorm_rope_quant_fp8(qkv, gq, gk, grid, w.heads, out=f8)  # norm + RoPE + amax, quantise
+            if ev: ev[1].record(stream)
             if ev: ev[2].record(stream)
+        else:
+            wan_attn.qknorm_rope(qkv, gq, gk, grid, w.heads)
+            if ev: ev[1].record(stream)
+            if fp8:
+                wan_attn.qkv_quant_fp8(qkv, w.heads, out=f8)
+            if ev: ev[2].record(stream)
+        if fp8:
             wan_attn.attn_fwd_fp8(f8, out=out)
         else:
-            if ev: ev[2].record(stream)
             wan_attn.attn_fwd(qkv, w.heads, out=out)
         if ev: ev[3].record(stream)
 
@@ -242,7 +251,16 @@ def main():
                         "bytes_per_launch": w.norm_bytes(),
                         "traffic": committed_traffic("qknorm_rope", w.name)},
     }
-    if fp8:
+    if fp8 and not args.fp8_unfused:
+        # one call: norm + RoPE + amax (reads Q, K, V; writes Q, K), then the
+        # quantisation (reads Q, K, V; writes e4m3 Q, K, V^T)
+        del rec["qknorm_rope"]
+        prep_bytes = w.B * w.S * w.D * (8 + 2 + 6 + 3)
+        rec["qknorm_rope_quant_fp8"] = {
+            "bound": "hbm", "achieved": round(prep_bytes / (norm_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(prep_bytes / (norm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "ms_per_launch": round(norm_ms, 4), "bytes_per_launch": prep_bytes}
+    elif fp8:
         rec["quant_ms_per_launch"] = round(quant_ms, 4)
     if args.ring_cp:
         ring = ring_share(w, qkv, args.ring_cp)

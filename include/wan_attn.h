@@ -12,7 +12,8 @@
  *     -> wan_attn_fwd    : bidirectional (unmasked) softmax attention of every
  *                          head over every token, read straight from the packed
  *                          buffer
- *   (fp8 variant: wan_qkv_quant_fp8, then wan_attn_fwd_fp8)
+ *   (fp8 variant: wan_qkv_quant_fp8, then wan_attn_fwd_fp8; or
+ *    wan_qknorm_rope_quant_fp8 in place of the first two steps)
  *
  * Sources (web pages on Wan2.2, cited by title and section):
  *   "Optimizing High-Quality Offline Video Generation" (AWS Neuron docs):
@@ -212,6 +213,29 @@ int wan_attn_merge(float *acc_out, float *acc_lse, const float *chunk_out, const
  */
 int wan_qkv_quant_fp8(const void *qkv, void *qk8, void *vt8, float *scales, float *amax,
                       int64_t B, int64_t S, int64_t heads, int64_t head_dim, void *stream);
+
+/*
+ * wan_qknorm_rope_quant_fp8 -- wan_qknorm_rope followed by wan_qkv_quant_fp8 on
+ * its result, with the amax step folded into the norm pass: while Q and K are
+ * normalised, rotated and written back (bf16, in place), the same pass takes
+ * max |x| of the values it writes and of V, so the quantisation needs no
+ * separate pass over the buffer to find them ("Optimize Wan2.2 Dataflow":
+ * change 2 fuses amax, E4M3 scale and quantisation into the producing kernel;
+ * here the producer is the fused Q/K norm + RoPE of the same pull request).
+ *
+ * Every output is bit-identical to the two calls in sequence with the same
+ * arguments: qkv (Q, K updated in place), qk8, vt8, scales and amax.
+ * Arguments: those of wan_qknorm_rope (qkv, gamma_q, gamma_k, B, T, H, W,
+ * heads, head_dim, eps, theta), then those of wan_qkv_quant_fp8 (qk8, vt8,
+ * scales, amax; S = T*H*W), then the stream. Three kernels on `stream`
+ * (clear amax, norm + RoPE + amax, quantise). Calls that share `amax` must
+ * not overlap in time.
+ * Errors: those of both calls; WAN_E_ALIAS also when a gamma overlaps an fp8
+ * output.
+ */
+int wan_qknorm_rope_quant_fp8(void *qkv, const void *gamma_q, const void *gamma_k, int64_t B, int64_t T,
+                              int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
+                              void *qk8, void *vt8, float *scales, float *amax, void *stream);
 
 /* Bytes of the vt8 buffer for (B, S, heads, head_dim); -1 on invalid sizes or
  * overflow. Pure host arithmetic. */

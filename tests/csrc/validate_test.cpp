@@ -101,6 +101,26 @@ int main() {
   EXPECT_EQ(validate_attn_fp8(qk8, vt8, sc, qk8 + 64, nullptr, 1, 16, 2, 128, 0.088f, &z), WAN_E_ALIAS);
   EXPECT_EQ(validate_attn_fp8(qk8, vt8, nullptr, outb, nullptr, 1, 16, 2, 128, 0.088f, &z), WAN_E_NULL);
   EXPECT_EQ(validate_attn_fp8(qk8, vt8, sc, outb, nullptr, 1, 16, 2, 128, -2.f, &z), WAN_E_VALUE);
+  // fused norm + quantisation: both sets of checks, and no gamma inside an fp8 output
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, qk8, vt8, sc, am, &z), WAN_OK);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, qk8 + 256, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, qk8, vt8, sc, am, &z),
+            WAN_E_ALIAS);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, g1, vt8, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, qk8, vt8, sc, am, &z),
+            WAN_E_ALIAS);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, qk8, vt8, sc, sc, &z),
+            WAN_E_ALIAS);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, buf + 512, vt8, sc, am, &z),
+            WAN_E_ALIAS);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, qk8, nullptr, sc, am, &z),
+            WAN_E_NULL);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, nullptr, g2, 1, 2, 8, 8, 2, 128, 1e-6f, 1e4f, qk8, vt8, sc, am, &z),
+            WAN_E_NULL);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, g1, g2, 1, 2, 8, 8, 2, 128, -1.f, 1e4f, qk8, vt8, sc, am, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_qknorm_rope_fp8(qkv, g1, g2, 70000, 2, 8, 8, 2, 128, 1e-6f, 1e4f, qk8, vt8, sc, am, &z),
+            WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_qknorm_rope_fp8(nullptr, nullptr, nullptr, 1, 0, 8, 8, 2, 128, 1e-6f, 1e4f, nullptr, nullptr,
+                                     nullptr, nullptr, &z),
+            WAN_OK);
   int64_t vtb = 0;
   EXPECT_EQ(fp8_vt_bytes(2, 129, 3, &vtb), 1);
   EXPECT_EQ(vtb, 2 * 3 * 128 * 256);

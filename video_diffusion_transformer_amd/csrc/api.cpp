@@ -98,10 +98,36 @@ int wan_qknorm_rope(void* qkv, const void* gamma_q, const void* gamma_k, int64_t
   for (int64_t r0 = 0; r0 < z.rows; r0 += kMaxRowsPerLaunch) {
     const int64_t n = z.rows - r0 < kMaxRowsPerLaunch ? z.rows - r0 : kMaxRowsPerLaunch;
     if (wan::launch_qknorm_rope(qkv, gamma_q, gamma_k, tab, r0, n, static_cast<int>(z.S), static_cast<int>(T),
-                                static_cast<int>(H), static_cast<int>(W), static_cast<int>(z.D), eps,
+                                static_cast<int>(H), static_cast<int>(W), static_cast<int>(z.D), eps, nullptr,
                                 st) != hipSuccess)
       return WAN_E_HIP;
   }
+  return WAN_OK;
+}
+
+int wan_qknorm_rope_quant_fp8(void* qkv, const void* gamma_q, const void* gamma_k, int64_t B, int64_t T, int64_t H,
+                              int64_t W, int64_t heads, int64_t head_dim, float eps, float theta, void* qk8,
+                              void* vt8, float* scales, float* amax, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_qknorm_rope_fp8(qkv, gamma_q, gamma_k, B, T, H, W, heads, head_dim, eps, theta, qk8, vt8,
+                                         scales, amax, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (T > INT32_MAX / 22 || H > INT32_MAX / 21 || W > INT32_MAX / 21) return WAN_E_OVERFLOW;
+  const float2* tab = nullptr;
+  rc = rope_table(T, H, W, theta, &tab);
+  if (rc != WAN_OK) return rc;
+  auto st = static_cast<hipStream_t>(stream);
+  if (wan::launch_amax_clear(amax, st) != hipSuccess) return WAN_E_HIP;
+  for (int64_t r0 = 0; r0 < z.rows; r0 += kMaxRowsPerLaunch) {
+    const int64_t n = z.rows - r0 < kMaxRowsPerLaunch ? z.rows - r0 : kMaxRowsPerLaunch;
+    if (wan::launch_qknorm_rope(qkv, gamma_q, gamma_k, tab, r0, n, static_cast<int>(z.S), static_cast<int>(T),
+                                static_cast<int>(H), static_cast<int>(W), static_cast<int>(z.D), eps, amax,
+                                st) != hipSuccess)
+      return WAN_E_HIP;
+  }
+  if (wan::launch_quant_fp8(qkv, qk8, vt8, scales, amax, static_cast<int>(B), static_cast<int>(z.S),
+                            static_cast<int>(heads), st) != hipSuccess)
+    return WAN_E_HIP;
   return WAN_OK;
 }
 

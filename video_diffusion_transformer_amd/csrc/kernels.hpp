@@ -9,9 +9,12 @@ namespace wan {
 // Q/K RMSNorm + bf16 + 3-D RoPE, in place, rows [row0, row0 + rows) of the
 // packed buffer. `tab` holds the fp32 (cos, sin) pairs: frame axis [T][22],
 // then row axis [H][21], then column axis [W][21].
+// With amax non-null the kernel also folds max |x| of the rounded Q and K it
+// writes and of V into amax[0..2] (atomic maxima on the float bits; the caller
+// clears them first).
 hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const float2* tab,
                               int64_t row0, int64_t rows, int S, int T, int H, int W, int D,
-                              float eps, hipStream_t stream);
+                              float eps, float* amax, hipStream_t stream);
 
 // bf16 attention forward over the packed buffer.
 hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S, int heads,
@@ -30,6 +33,10 @@ hipError_t launch_attn_merge(float* acc, float* acc_lse, const float* chunk, con
 // vt8 [B, heads, 128, S_pad] (V transposed per head, zero past S).
 hipError_t launch_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int B, int S,
                                 int heads, hipStream_t stream);
+// The two halves of it: clearing amax, and the quantisation given amax.
+hipError_t launch_amax_clear(float* amax, hipStream_t stream);
+hipError_t launch_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, const float* amax, int B, int S,
+                            int heads, hipStream_t stream);
 
 // fp8 attention forward from the quantised buffers.
 hipError_t launch_attn_fwd_fp8(const void* qk8, const void* vt8, const float* scales, void* out, float* lse, int B,

@@ -9,7 +9,13 @@
 // halves. Q and K stay in registers between the reduction and the store: every
 // element is read once and written once (HBM-bound, ~2 FLOP/byte). The full-width
 // mean square is a wavefront butterfly reduction followed by a cross-wave sum in
-// LDS. V is never touched.
+// LDS. V is never written.
+//
+// The fp8 variant (Amax) also takes, in the same pass, max |x| of the rounded Q
+// and K it writes and of V (read once for it), and folds them into amax[0..2]:
+// the amax step of the amax -> E4M3 scale -> quantise recipe ("Optimize Wan2.2
+// Dataflow", change 2) moved into the norm epilogue, so the quantisation pass
+// that follows needs no separate amax pass over Q, K and V.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,11 +25,23 @@ namespace {
 
 constexpr int kPairsT = 22, kPairsH = 21, kPairsW = 21;  // 44/42/42 channels per axis
 
-template <int CPT>
+__device__ __forceinline__ float absmax8(float m, const u32x4_t v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[j])), fabsf(bf16_hi(v[j]))));
+  return m;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+template <int CPT, bool Amax>
 __global__ void __launch_bounds__(1024)
 qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
                    const uint16_t* __restrict__ gk, const float2* __restrict__ tab, int64_t row0,
-                   int S, int H, int W, int D, int offH, int offW, float inv_d, float eps) {
+                   int S, int H, int W, int D, int offH, int offW, float inv_d, float eps, float* __restrict__ amax) {
   const int64_t row = row0 + blockIdx.x;
   const int s = static_cast<int>(row % S);
   const int f = s / (H * W), y = (s / W) % H, x = s % W;
@@ -32,7 +50,7 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
   uint16_t* krow = qrow + D;
 
   u32x4_t qv[CPT], kv[CPT];
-  float sq = 0.f, sk = 0.f;
+  float sq = 0.f, sk = 0.f, mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + i * blockDim.x;
@@ -44,6 +62,7 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
       qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * c);
       kv[i] = *reinterpret_cast<const u32x4_t*>(krow + 8 * c);
 #endif
+      if constexpr (Amax) mv = absmax8(mv, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + D + 8 * c)));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float a = bf16_lo(qv[i][j]), b = bf16_hi(qv[i][j]);
@@ -100,6 +119,10 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
         b = bf16_hi(nk);
         ko[j] = pack_bf16x2(a * cs.x - b * cs.y, a * cs.y + b * cs.x);
       }
+      if constexpr (Amax) {
+        mq = absmax8(mq, qo);
+        mk = absmax8(mk, ko);
+      }
 #if WAN_NORM_NT & 2
       __builtin_nontemporal_store(qo, reinterpret_cast<u32x4_t*>(qrow + 8 * c));
       __builtin_nontemporal_store(ko, reinterpret_cast<u32x4_t*>(krow + 8 * c));
@@ -109,13 +132,35 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
 #endif
     }
   }
+  if constexpr (Amax) {
+    // Block maxima, then one atomic maximum per tensor (non-negative floats
+    // order like their bits). Most blocks find the running value already
+    // larger and skip the atomic.
+    __shared__ float pmax[32][3];
+    mq = wave_max(mq);
+    mk = wave_max(mk);
+    mv = wave_max(mv);
+    if ((threadIdx.x & 63) == 0) {
+      pmax[wave][0] = mq;
+      pmax[wave][1] = mk;
+      pmax[wave][2] = mv;
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+      float m = 0.f;
+      for (int w = 0; w < nwaves; ++w) m = fmaxf(m, pmax[w][threadIdx.x]);
+      unsigned* p = reinterpret_cast<unsigned*>(amax) + threadIdx.x;
+      const unsigned bits = __float_as_uint(m);
+      if (bits > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, bits);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const float2* tab,
                               int64_t row0, int64_t rows, int S, int T, int H, int W, int D,
-                              float eps, hipStream_t stream) {
+                              float eps, float* amax, hipStream_t stream) {
 #ifndef WAN_NORM_MIN_CPT
 #define WAN_NORM_MIN_CPT 2  // two 16-byte chunks of Q and of K per thread: more bytes in flight per CU
 #endif
@@ -133,12 +178,19 @@ hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const f
   auto* a = static_cast<const uint16_t*>(gq);
   auto* b = static_cast<const uint16_t*>(gk);
   dim3 grid(static_cast<unsigned>(rows));
-  if (cpt == 1)
-    hipLaunchKernelGGL(qknorm_rope_kernel<1>, grid, dim3(threads), 0, stream, q, a, b, tab, row0, S, H, W, D, offH, offW, inv_d, eps);
-  else if (cpt == 2)
-    hipLaunchKernelGGL(qknorm_rope_kernel<2>, grid, dim3(threads), 0, stream, q, a, b, tab, row0, S, H, W, D, offH, offW, inv_d, eps);
-  else
-    hipLaunchKernelGGL(qknorm_rope_kernel<4>, grid, dim3(threads), 0, stream, q, a, b, tab, row0, S, H, W, D, offH, offW, inv_d, eps);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, q, a, b, tab, row0, S, H, W, D, offH, offW, inv_d, eps,
+                       amax);
+  };
+  if (amax) {
+    if (cpt == 1) go(qknorm_rope_kernel<1, true>);
+    else if (cpt == 2) go(qknorm_rope_kernel<2, true>);
+    else go(qknorm_rope_kernel<4, true>);
+  } else {
+    if (cpt == 1) go(qknorm_rope_kernel<1, false>);
+    else if (cpt == 2) go(qknorm_rope_kernel<2, false>);
+    else go(qknorm_rope_kernel<4, false>);
+  }
   return hipGetLastError();
 }
 

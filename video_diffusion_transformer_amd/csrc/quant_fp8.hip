@@ -127,19 +127,29 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
 
 }  // namespace
 
-hipError_t launch_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int B, int S,
-                                int heads, hipStream_t stream) {
-  const int D = heads * 128;
-  const int64_t rows = (int64_t)B * S;
-  const int S_pad = (S + 127) / 128 * 128;
+hipError_t launch_amax_clear(float* amax, hipStream_t stream) {
   hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(64), 0, stream, amax);
-  const int64_t nb = rows < 8192 ? rows : 8192;
-  hipLaunchKernelGGL(amax_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(qkv), amax, rows, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, const float* amax, int B, int S,
+                            int heads, hipStream_t stream) {
+  const int S_pad = (S + 127) / 128 * 128;
   hipLaunchKernelGGL(quant_kernel, dim3(S_pad / kTok, heads, B), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qkv), static_cast<uint8_t*>(qk8), static_cast<uint8_t*>(vt8),
                      amax, scales, S, S_pad, heads);
   return hipGetLastError();
+}
+
+hipError_t launch_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, float* amax, int B, int S,
+                                int heads, hipStream_t stream) {
+  const int D = heads * 128;
+  const int64_t rows = (int64_t)B * S;
+  hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(64), 0, stream, amax);
+  const int64_t nb = rows < 8192 ? rows : 8192;
+  hipLaunchKernelGGL(amax_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qkv), amax, rows, D);
+  return launch_quant_fp8(qkv, qk8, vt8, scales, amax, B, S, heads, stream);
 }
 
 }  // namespace wan

@@ -174,6 +174,24 @@ inline int validate_quant_fp8(const void* qkv, const void* qk8, const void* vt8,
   return WAN_OK;
 }
 
+// Norm + RoPE in place followed by the fp8 quantisation of the result: the
+// checks of both calls, plus the gammas must not overlap an fp8 output.
+inline int validate_qknorm_rope_fp8(const void* qkv, const void* gq, const void* gk, int64_t B, int64_t T,
+                                    int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
+                                    const void* qk8, const void* vt8, const void* scales, const void* amax, Sizes* z) {
+  int rc = validate_qknorm_rope(qkv, gq, gk, B, T, H, W, heads, head_dim, eps, theta, z);
+  if (rc != WAN_OK) return rc;
+  rc = validate_quant_fp8(qkv, qk8, vt8, scales, amax, B, z->S, heads, head_dim, z);
+  if (rc != WAN_OK || z->empty) return rc;
+  int64_t vt_bytes;
+  fp8_vt_bytes(B, z->S, heads, &vt_bytes);
+  const void* outs[4] = {qk8, vt8, scales, amax};
+  const int64_t sizes[4] = {z->rows * 2 * z->D, vt_bytes, 12, 12};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(outs[i], sizes[i], gq, z->D * 2) || overlaps(outs[i], sizes[i], gk, z->D * 2)) return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 inline int validate_attn_fp8(const void* qk8, const void* vt8, const void* scales, const void* out,
                              const void* lse, int64_t B, int64_t S, int64_t heads, int64_t head_dim, float scale,
                              Sizes* z) {

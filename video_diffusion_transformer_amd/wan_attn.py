@@ -8,7 +8,7 @@ call raises -- nothing falls back to another implementation.
 The names follow the C ABI: ``qknorm_rope`` -> wan_qknorm_rope,
 ``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_chunk`` -> wan_attn_fwd_chunk,
 ``attn_merge`` -> wan_attn_merge, ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
-``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
+``qknorm_rope_quant_fp8`` -> wan_qknorm_rope_quant_fp8, ``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
 """
 
 import ctypes
@@ -39,6 +39,8 @@ SIGNATURES = {
     "wan_attn_fwd_chunk": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _P]),
     "wan_attn_merge": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qkv_quant_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "wan_qknorm_rope_quant_fp8": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F,
+                                                 _P, _P, _P, _P, _P]),
     "wan_fp8_vt_bytes": (ctypes.c_int64, [_I64, _I64, _I64, _I64]),
     "wan_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
 }
@@ -248,6 +250,34 @@ def qkv_quant_fp8(qkv, heads, head_dim=HEAD_DIM, out=None, stream=None):
         _check("wan_qkv_quant_fp8", lib().wan_qkv_quant_fp8(
             _ptr(qkv), _ptr(f.qk8), _ptr(f.vt8), _ptr(f.scales), _ptr(f.amax), B, S, heads, head_dim,
             _stream(qkv.device, stream)))
+    return f
+
+
+def qknorm_rope_quant_fp8(qkv, gamma_q, gamma_k, grid, heads, head_dim=HEAD_DIM, eps=RMS_EPS, theta=ROPE_THETA,
+                          out=None, stream=None):
+    """qknorm_rope (in place) and then qkv_quant_fp8 of the result, with the
+    amax folded into the norm pass. Returns an Fp8QKV (allocated unless
+    ``out`` is given)."""
+    T, H, W = grid
+    for name, t in (("qkv", qkv), ("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        _need_gpu(name, t, torch.bfloat16)
+    B, D = qkv.shape[0], heads * head_dim
+    S = T * H * W
+    if qkv.dim() != 3 or qkv.shape[1] != S or qkv.shape[2] != 3 * D:
+        raise ValueError(f"qkv must be [B, {S}, {3 * D}], got {tuple(qkv.shape)}")
+    if gamma_q.numel() != D or gamma_k.numel() != D:
+        raise ValueError("gammas must have heads*head_dim elements")
+    f = out if out is not None else fp8_buffers(B, S, heads, qkv.device, head_dim)
+    for name in ("qk8", "vt8"):
+        _need_gpu(name, getattr(f, name), torch.uint8)
+    _need_gpu("scales", f.scales, torch.float32)
+    _need_gpu("amax", f.amax, torch.float32)
+    if f.vt8.numel() < lib().wan_fp8_vt_bytes(B, S, heads, head_dim) or f.qk8.numel() != B * S * 2 * D:
+        raise ValueError("fp8 buffers are too small for these sizes")
+    with torch.cuda.device(qkv.device):
+        _check("wan_qknorm_rope_quant_fp8", lib().wan_qknorm_rope_quant_fp8(
+            _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), B, T, H, W, heads, head_dim, eps, theta,
+            _ptr(f.qk8), _ptr(f.vt8), _ptr(f.scales), _ptr(f.amax), _stream(qkv.device, stream)))
     return f
 
 
