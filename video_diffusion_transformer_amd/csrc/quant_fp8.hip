@@ -19,7 +19,10 @@ namespace wan {
 
 namespace {
 
-constexpr int kTok = 64;  // tokens per quantisation tile
+#ifndef WAN_QUANT_TOK
+#define WAN_QUANT_TOK 128
+#endif
+constexpr int kTok = WAN_QUANT_TOK;  // tokens per quantisation tile: 128 keys fill whole 128-byte lines of V^T
 
 __global__ void amax_clear_kernel(float* amax) {
   if (threadIdx.x < 3) amax[threadIdx.x] = 0.f;
@@ -79,7 +82,7 @@ __device__ __forceinline__ uint2 quant8(const u32x4_t v, float s) {
   return make_uint2(w[0], w[1]);
 }
 
-// One block = 64 tokens of one (b, head): Q and K rows are quantised in place
+// One block = kTok tokens of one (b, head): Q and K rows are quantised in place
 // of their packed position; V goes through LDS to be stored channel-major.
 __global__ void __launch_bounds__(256)
 quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_t* __restrict__ vt8,
@@ -93,9 +96,9 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
     scales[1] = sk;
     scales[2] = sv;
   }
-  // 64 tokens x 16 chunks of 8 channels = 1024 chunks, 4 per thread.
+  // kTok tokens x 16 chunks of 8 channels, kTok / 16 per thread.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kTok / 16; ++i) {
     const int c = threadIdx.x + 256 * i;
     const int t = c >> 4, ch = c & 15;
     const int s = s0 + t;
@@ -114,12 +117,13 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
     }
   }
   __syncthreads();
-  // 128 channel rows x 64 keys = 128 x 4 chunks of 16 B, 2 per thread.
+  // 128 channel rows x kTok keys = 128 x (kTok / 16) chunks of 16 B.
   uint8_t* vbase = vt8 + (((int64_t)b * heads + h) * 128) * S_pad + s0;
+  constexpr int kParts = kTok / 16;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kParts / 2; ++i) {
     const int c = threadIdx.x + 256 * i;
-    const int d = c >> 2, part = c & 3;
+    const int d = c / kParts, part = c % kParts;
     *reinterpret_cast<u32x4_t*>(vbase + (int64_t)d * S_pad + 16 * part) =
         *reinterpret_cast<const u32x4_t*>(&vt[d][16 * part]);
   }
