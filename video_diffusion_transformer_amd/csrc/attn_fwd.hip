@@ -100,6 +100,7 @@ struct TileArgs {
 // tile's first row are fixed (gk, gv); only the last tile, whose rows past the
 // end re-read row S-1 (masked later), recomputes them.
 constexpr int kBlk = 16 / kWaves;  // 1 KB blocks per wave per K or V tile
+static_assert(16 % kWaves == 0, "the 16 blocks of a K or V tile must split evenly over the waves");
 
 __device__ __forceinline__ int tile_row(const TileArgs& a, int j) { return 4 * (kBlk * a.wave + j) + (a.lane >> 4); }
 

@@ -46,6 +46,7 @@ constexpr int kBN = 128;                 // keys per unit
 #endif
 constexpr int kWaves = WAN_FP8_WAVES;
 constexpr int kThreads = 64 * kWaves;
+static_assert(16 % kWaves == 0, "the 16 blocks of a K or V^T tile must split evenly over the waves");
 constexpr int kBM = 32 * kWaves;
 constexpr int kTile = 128 * 128;         // bytes of one K or V^T tile
 constexpr int kStage = 2 * kTile;
