@@ -21,8 +21,8 @@ line is printed.
               the same workload (query rows of one head against all keys).
   ring_share  (bf16 workloads) one GPU's share of ring attention with the
               sequence split over --ring-cp ranks: S/cp queries against cp
-              K/V chunks, each followed by the log-sum-exp merge; not part of
-              the step or of value.
+              K/V chunks, each round folded into the accumulator by the
+              log-sum-exp merge; not part of the step or of value.
 """
 
 import argparse
@@ -90,9 +90,11 @@ def cpu_baseline(w, budget_s=12.0):
 
 def ring_share(w, qkv, cp, reps=3):
     """One GPU's share of a ring-attention call with the sequence split over cp
-    ranks: its S/cp queries attend each of the cp K/V chunks (wan_attn_fwd_chunk)
-    and the partial results are folded by the log-sum-exp merge (wan_attn_merge).
-    Times reps whole shares after one warm-up, with HIP events on the stream."""
+    ranks: its S/cp queries attend each of the cp K/V chunks, each round folded
+    into the accumulator in the attention epilogue (wan_attn_fwd_chunk_merge).
+    Also times the same share with the chunk output written out and merged by
+    the separate kernel (wan_attn_fwd_chunk + wan_attn_merge). HIP events on
+    the stream, reps shares after one warm-up each."""
     import torch
 
     from video_diffusion_transformer_amd import wan_attn
@@ -111,32 +113,36 @@ def ring_share(w, qkv, cp, reps=3):
     stream = torch.cuda.current_stream(dev)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def share(ev=None):
+    def fused():
         acc_lse.fill_(-math.inf)  # empty accumulator
         for c in range(cp):
-            wan_attn.attn_fwd_chunk(shard, chunks[c], w.heads, out=o, lse=lse)
-            if ev: ev[c][0].record(stream)
-            wan_attn.attn_merge(acc, acc_lse, o, lse, w.heads, out_bf16=out16 if c == cp - 1 else None)
-            if ev: ev[c][1].record(stream)
+            wan_attn.attn_fwd_chunk_merge(shard, chunks[c], acc, acc_lse, w.heads,
+                                          out_bf16=out16 if c == cp - 1 else None)
 
-    share()
-    torch.cuda.synchronize()
-    evs = [[[E(), E()] for _ in range(cp)] for _ in range(reps)]
-    t0, t1 = E(), E()
-    t0.record(stream)
-    for r in range(reps):
-        share(evs[r])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / reps
-    merge_ms = sum(e[0].elapsed_time(e[1]) for ev in evs for e in ev) / (reps * cp)
+    def separate():
+        acc_lse.fill_(-math.inf)
+        for c in range(cp):
+            wan_attn.attn_fwd_chunk(shard, chunks[c], w.heads, out=o, lse=lse)
+            wan_attn.attn_merge(acc, acc_lse, o, lse, w.heads, out_bf16=out16 if c == cp - 1 else None)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = E(), E()
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    ms = timed(fused)
+    ms_sep = timed(separate)
     flop = 4.0 * w.B * w.heads * sq * w.S * 128
-    merge_bytes = w.B * sq * w.D * 4 * 3 + w.B * w.heads * sq * 4 * 3  # read acc + chunk, write acc; LSEs
     return {"cp": cp, "queries": sq, "ms_per_share": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
-            "merge_ms_per_call": round(merge_ms, 4),
-            "merge_gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
-            "note": "attention of S/cp local queries against cp K/V chunks of S/cp keys + cp merges; "
-                    "TFLOP/s counts the attention FLOP of the share over the whole share time"}
+            "ms_per_share_separate_merge": round(ms_sep, 4),
+            "note": "S/cp local queries against cp K/V chunks of S/cp keys, each round merged in the attention "
+                    "epilogue; TFLOP/s counts the attention FLOP of the share over the whole share time"}
 
 
 def main():

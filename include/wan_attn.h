@@ -185,6 +185,26 @@ int wan_attn_merge(float *acc_out, float *acc_lse, const float *chunk_out, const
                    void *stream);
 
 /*
+ * wan_attn_fwd_chunk_merge -- one ring round with the merge done in the
+ * attention epilogue: the queries of q_src attend the chunk of kv_src, and the
+ * result is folded straight into the accumulator with the wan_attn_merge
+ * formula, bit-identical to wan_attn_fwd_chunk followed by wan_attn_merge (the
+ * chunk's fp32 output is never written). Same sources as those two calls.
+ *
+ *   q_src, kv_src, Sq, Skv, B, heads, head_dim, softmax_scale: as
+ *              wan_attn_fwd_chunk.
+ *   acc_out    fp32 [B, Sq, D] in/out;  acc_lse  fp32 [B, heads, Sq] in/out
+ *              (required; an LSE of -inf marks an empty row, whose acc_out is
+ *              not read).
+ *   out_bf16   bf16 [B, Sq, D] copy of the merged output, or NULL.
+ * acc_out, acc_lse and out_bf16 must not overlap the inputs or each other.
+ * Errors: as wan_attn_fwd_chunk, plus WAN_E_ALIAS / WAN_E_ALIGN for out_bf16.
+ */
+int wan_attn_fwd_chunk_merge(const void *q_src, int64_t Sq, const void *kv_src, int64_t Skv,
+                             float *acc_out, float *acc_lse, void *out_bf16, int64_t B, int64_t heads,
+                             int64_t head_dim, float softmax_scale, void *stream);
+
+/*
  * wan_qkv_quant_fp8 -- per-tensor e4m3 quantisation of Q, K and V for the fp8
  * attention path (the amax -> E4M3 scale -> quantise recipe of "Optimize Wan2.2
  * Dataflow", change 2, applied to the attention inputs; the pull request's

@@ -88,6 +88,15 @@ int main() {
   EXPECT_EQ(validate_attn_merge(of32, lsea, of32b, nullptr, nullptr, 1, 16, 2, 128, &z), WAN_E_NULL);
   EXPECT_EQ(validate_attn_merge(of32 + 1, lsea, of32b, lsec, nullptr, 1, 16, 2, 128, &z), WAN_E_ALIGN);
 
+  // one ring round folded into the accumulator
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, outb, 1, 16, 16, 2, 128, 0.088f, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, nullptr, 1, 16, 16, 2, 128, 0.088f, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, buf + 512, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, of32 + 64, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, outb + 8, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_ALIGN);
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, nullptr, outb, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, outb, 1, 16, 0, 2, 128, 0.088f, &z), WAN_E_SHAPE);
+
   // fp8 quantisation and attention
   alignas(16) static unsigned char qk8[1 << 16], vt8[1 << 16];
   alignas(16) static float sc[4], am[4];

@@ -107,6 +107,48 @@ def test_merge_into_empty_accumulator_ignores_its_contents():
     assert torch.equal(out16, o.to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("B,S,heads,bounds", [(1, 500, 2, [0, 130, 333, 500]), (2, 777, 3, [0, 1, 400, 777]),
+                                              (1, 300, 40, [0, 150, 300])])
+def test_chunk_merge_equals_chunk_then_merge(B, S, heads, bounds):
+    """The merge in the attention epilogue gives the same bits as the chunk
+    output merged by the separate kernel, round after round (the first round
+    into a NaN-filled empty accumulator)."""
+    D = heads * 128
+    qkv = synth.make_qkv(B, S, heads, seed=S + 2 * heads).to(DEV)
+    a_acc = torch.full((B, S, D), math.nan, dtype=torch.float32, device=DEV)
+    b_acc = a_acc.clone()
+    a_lse = torch.full((B, heads, S), -math.inf, dtype=torch.float32, device=DEV)
+    b_lse = a_lse.clone()
+    a16 = torch.empty((B, S, D), dtype=torch.bfloat16, device=DEV)
+    b16 = torch.empty_like(a16)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        kv = qkv[:, lo:hi].contiguous()
+        o, l = wan_attn.attn_fwd_chunk(qkv, kv, heads)
+        wan_attn.attn_merge(a_acc, a_lse, o, l, heads, out_bf16=a16)
+        wan_attn.attn_fwd_chunk_merge(qkv, kv, b_acc, b_lse, heads, out_bf16=b16)
+        torch.cuda.synchronize()
+        assert torch.equal(a_acc, b_acc) and torch.equal(a_lse, b_lse) and torch.equal(a16, b16), (lo, hi)
+    o_ref, l_ref = wan_ref.attn_packed_ref(_np(qkv), heads, 128, SCALE)
+    assert_gates(attn_error_stats(_np(b16), o_ref), BF16_GATES, "folded bf16")
+    assert np.abs(_np(b_lse) - l_ref).max() <= LSE_ABS
+
+
+def test_chunk_merge_errors():
+    buf = torch.zeros(2 * 8 * 768, dtype=torch.bfloat16, device=DEV)
+    q = buf[:8 * 768].view(1, 8, 768)
+    acc = torch.zeros((1, 8, 256), dtype=torch.float32, device=DEV)
+    lse = torch.full((1, 2, 8), -math.inf, dtype=torch.float32, device=DEV)
+    with pytest.raises(wan_attn.WanError) as e:  # the bf16 copy inside the queries' buffer
+        wan_attn.attn_fwd_chunk_merge(q, q, acc, lse, 2, out_bf16=buf[3008:3008 + 2048].view(1, 8, 256))
+    assert e.value.status == -5
+    with pytest.raises(wan_attn.WanError) as e:  # no keys
+        wan_attn.attn_fwd_chunk_merge(q, torch.zeros((1, 0, 768), dtype=torch.bfloat16, device=DEV), acc, lse, 2)
+    assert e.value.status == -2
+    with pytest.raises(wan_attn.WanError) as e:  # accumulator and its LSE overlap
+        wan_attn.attn_fwd_chunk_merge(q, q, acc, acc.view(-1)[:16].view(1, 2, 8), 2)
+    assert e.value.status == -5
+
+
 def test_chunk_errors():
     q = torch.zeros((1, 8, 768), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(wan_attn.WanError) as e:

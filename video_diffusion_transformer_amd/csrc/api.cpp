@@ -156,6 +156,21 @@ int wan_attn_fwd_chunk(const void* q_src, int64_t Sq, const void* kv_src, int64_
   return WAN_OK;
 }
 
+int wan_attn_fwd_chunk_merge(const void* q_src, int64_t Sq, const void* kv_src, int64_t Skv, float* acc_out,
+                             float* acc_lse, void* out_bf16, int64_t B, int64_t heads, int64_t head_dim,
+                             float softmax_scale, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_attn_chunk_fold(q_src, kv_src, acc_out, acc_lse, out_bf16, B, Sq, Skv, heads, head_dim,
+                                         softmax_scale, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (B > INT32_MAX) return WAN_E_OVERFLOW;
+  if (wan::launch_attn_fwd_chunk_fold(q_src, static_cast<int>(Sq), kv_src, static_cast<int>(Skv), acc_out, acc_lse,
+                                      out_bf16, static_cast<int>(B), static_cast<int>(heads), softmax_scale,
+                                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
 int wan_attn_merge(float* acc_out, float* acc_lse, const float* chunk_out, const float* chunk_lse, void* out_bf16,
                    int64_t B, int64_t Sq, int64_t heads, int64_t head_dim, void* stream) {
   wan::Sizes z;

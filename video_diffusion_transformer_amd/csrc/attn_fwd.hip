@@ -256,12 +256,17 @@ __device__ __forceinline__ void tile_pv(const TileArgs& a, const unsigned char* 
 
 // Queries come from the Q part of one packed buffer (Sq rows per batch entry),
 // keys and values from the K and V parts of another (Skv rows); for full
-// attention both are the same buffer. F32Out selects an fp32 output (the
-// chunked path, whose partial outputs are merged later) instead of bf16.
-template <bool F32Out>
+// attention both are the same buffer. The output mode: bf16 O (full
+// attention); fp32 O and the LSE of this key chunk (one ring round); or the
+// chunk's result folded straight into an fp32 accumulator and its LSE (one ring
+// round with the merge in the epilogue, out16 optionally receiving a bf16 copy).
+enum OutMode { kOutBf16 = 0, kOutF32 = 1, kOutFold = 2 };
+
+template <int Mode>
 __global__ void __launch_bounds__(kThreads, (kQT >= 4 || kWaves > 4) ? 1 : 2)
 attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ kvsrc, void* __restrict__ out,
-                float* __restrict__ lse, int Sq, int S, int heads, int nqt, float scale_log2) {
+                float* __restrict__ lse, uint16_t* __restrict__ out16, int Sq, int S, int heads, int nqt,
+                float scale_log2) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStage];
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -360,7 +365,31 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
     const int q = q0 + 16 * u + l16;
     if (q < Sq) {
       const float inv = 1.0f / l_tot;
-      if constexpr (F32Out) {
+      if constexpr (Mode == kOutFold) {
+        const int64_t li = (int64_t)bh * Sq + q;
+        const LseFold fo = lse_fold(lse[li], (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f);
+        const int64_t o0 = ((int64_t)b * Sq + q) * D + h * kD + 4 * grp;
+        float* op = static_cast<float*>(out) + o0;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const f32x4_t c = acc_o[dt][u] * inv;
+          const f32x4_t av = fo.acc_empty ? f32x4_t{} : *reinterpret_cast<const f32x4_t*>(op + 16 * dt);
+          f32x4_t r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = lse_fold_value(fo, av[i], c[i]);
+          *reinterpret_cast<f32x4_t*>(op + 16 * dt) = r;
+          if (out16) {
+            uint2 w;
+            w.x = pack_bf16x2(r[0], r[1]);
+            w.y = pack_bf16x2(r[2], r[3]);
+            *reinterpret_cast<uint2*>(out16 + o0 + 16 * dt) = w;
+          }
+        }
+        // every lane of the query has read the old LSE above (same wave, earlier)
+        if (grp == 0) lse[li] = fo.L;
+        continue;
+      }
+      if constexpr (Mode == kOutF32) {
         float* op = static_cast<float*>(out) + ((int64_t)b * Sq + q) * D + h * kD + 4 * grp;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
@@ -389,8 +418,8 @@ hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S,
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   const auto* src = static_cast<const uint16_t*>(qkv);
-  hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream, src, src,
-                     out, lse, S, S, heads, nqt, scale_log2);
+  hipLaunchKernelGGL(attn_fwd_kernel<kOutBf16>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream, src,
+                     src, out, lse, nullptr, S, S, heads, nqt, scale_log2);
   return hipGetLastError();
 }
 
@@ -400,9 +429,22 @@ hipError_t launch_attn_fwd_chunk(const void* q_src, int Sq, const void* kv_src, 
   const int64_t nblocks = (int64_t)nqt * heads * B;
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), out, lse, Sq, Skv,
-                     heads, nqt, scale_log2);
+  hipLaunchKernelGGL(attn_fwd_kernel<kOutF32>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), out, lse, nullptr, Sq,
+                     Skv, heads, nqt, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_chunk_fold(const void* q_src, int Sq, const void* kv_src, int Skv, float* acc,
+                                      float* acc_lse, void* out16, int B, int heads, float softmax_scale,
+                                      hipStream_t stream) {
+  const int nqt = (Sq + kBM - 1) / kBM;
+  const int64_t nblocks = (int64_t)nqt * heads * B;
+  if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_fwd_kernel<kOutFold>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), acc, acc_lse,
+                     static_cast<uint16_t*>(out16), Sq, Skv, heads, nqt, scale_log2);
   return hipGetLastError();
 }
 

@@ -25,21 +25,16 @@ attn_merge_kernel(float* __restrict__ acc, float* __restrict__ acc_lse, const fl
   const int64_t row = g / heads;  // b * Sq + s
   const int64_t b = row / Sq, s = row % Sq;
   const int64_t li = (b * heads + h) * Sq + s;
-  const float la = acc_lse[li], lc = clse[li];
-  const float mx = fmaxf(la, lc);
-  // log(exp(la) + exp(lc)), safe when one side is -inf (an empty accumulator)
-  const float L = mx == -INFINITY ? -INFINITY : mx + log1pf(expf(-fabsf(la - lc)));
-  const float wa = la == -INFINITY ? 0.f : expf(la - L);
-  const float wc = lc == -INFINITY ? 0.f : expf(lc - L);
+  const LseFold fo = lse_fold(acc_lse[li], clse[li]);
   const int64_t off = row * (int64_t)heads * 128 + h * 128 + 2 * lane;
   // An empty accumulator row is not read: whatever it holds (e.g. a fresh
   // allocation) must not leak into the result through 0 * NaN.
-  const float2 a = la == -INFINITY ? make_float2(0.f, 0.f) : *reinterpret_cast<const float2*>(acc + off);
+  const float2 a = fo.acc_empty ? make_float2(0.f, 0.f) : *reinterpret_cast<const float2*>(acc + off);
   const float2 c = *reinterpret_cast<const float2*>(co + off);
-  const float2 r = make_float2(wa * a.x + wc * c.x, wa * a.y + wc * c.y);
+  const float2 r = make_float2(lse_fold_value(fo, a.x, c.x), lse_fold_value(fo, a.y, c.y));
   *reinterpret_cast<float2*>(acc + off) = r;
   if (out16) *reinterpret_cast<uint32_t*>(out16 + off) = pack_bf16x2(r.x, r.y);
-  if (lane == 0) acc_lse[li] = L;
+  if (lane == 0) acc_lse[li] = fo.L;
 }
 
 }  // namespace

@@ -33,6 +33,29 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
 }
 
+// Fold of two partial attentions over disjoint key sets (natural-log LSEs la of
+// the accumulator, lc of the chunk): L = log(e^la + e^lc), and the accumulator
+// becomes wa * acc + wc * chunk with wa = e^(la - L), wc = e^(lc - L). An LSE of
+// -inf is an empty side (weight 0; an empty accumulator is not read). Shared by
+// the merge kernel and the merging epilogue of the chunk attention, so the two
+// give the same bits.
+struct LseFold {
+  float L, wa, wc;
+  bool acc_empty;
+};
+__device__ __forceinline__ LseFold lse_fold(float la, float lc) {
+  const float mx = fmaxf(la, lc);
+  LseFold f;
+  f.L = mx == -INFINITY ? -INFINITY : mx + log1pf(expf(-fabsf(la - lc)));
+  f.acc_empty = la == -INFINITY;
+  f.wa = f.acc_empty ? 0.f : expf(la - f.L);
+  f.wc = lc == -INFINITY ? 0.f : expf(lc - f.L);
+  return f;
+}
+__device__ __forceinline__ float lse_fold_value(const LseFold& f, float a, float c) {
+  return fmaf(f.wa, f.acc_empty ? 0.f : a, f.wc * c);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -26,6 +26,9 @@ hipError_t launch_attn_fwd_chunk(const void* q_src, int Sq, const void* kv_src, 
                                  int heads, float softmax_scale, hipStream_t stream);
 
 // In-place log-sum-exp merge of a chunk result into an accumulator.
+hipError_t launch_attn_fwd_chunk_fold(const void* q_src, int Sq, const void* kv_src, int Skv, float* acc,
+                                      float* acc_lse, void* out16, int B, int heads, float softmax_scale,
+                                      hipStream_t stream);
 hipError_t launch_attn_merge(float* acc, float* acc_lse, const float* chunk, const float* chunk_lse, void* out16,
                              int B, int Sq, int heads, hipStream_t stream);
 

@@ -142,6 +142,24 @@ inline int validate_attn_merge(const void* acc, const void* acc_lse, const void*
   return WAN_OK;
 }
 
+// One ring round folded into the accumulator: the chunk checks for the inputs,
+// and acc, acc_lse, out16 (optional) distinct from the inputs and each other.
+inline int validate_attn_chunk_fold(const void* q_src, const void* kv_src, const void* acc, const void* acc_lse,
+                                    const void* out16, int64_t B, int64_t Sq, int64_t Skv, int64_t heads,
+                                    int64_t head_dim, float scale, Sizes* z) {
+  int rc = validate_attn_chunk(q_src, kv_src, acc, acc_lse, B, Sq, Skv, heads, head_dim, scale, z);
+  if (rc != WAN_OK || z->empty) return rc;
+  if (out16 && !aligned(out16, 16)) return WAN_E_ALIGN;
+  int64_t kv_bytes;
+  mul_ok(B * Skv, 3 * z->D, &kv_bytes);
+  kv_bytes *= 2;
+  const int64_t h_bytes = z->out_elems * 2;
+  if (overlaps(out16, h_bytes, q_src, z->qkv_elems * 2) || overlaps(out16, h_bytes, kv_src, kv_bytes) ||
+      overlaps(out16, h_bytes, acc, z->out_elems * 4) || overlaps(out16, h_bytes, acc_lse, z->B * z->heads * z->S * 4))
+    return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 // Bytes of the transposed fp8 V buffer: B * heads * 128 * S_pad, S_pad = S rounded up to 128.
 inline bool fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t* out) {
   const int64_t s_pad = (S + 127) / 128 * 128;

@@ -7,7 +7,8 @@ call raises -- nothing falls back to another implementation.
 
 The names follow the C ABI: ``qknorm_rope`` -> wan_qknorm_rope,
 ``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_chunk`` -> wan_attn_fwd_chunk,
-``attn_merge`` -> wan_attn_merge, ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
+``attn_merge`` -> wan_attn_merge, ``attn_fwd_chunk_merge`` -> wan_attn_fwd_chunk_merge,
+``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
 ``qknorm_rope_quant_fp8`` -> wan_qknorm_rope_quant_fp8, ``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
 """
 
@@ -38,6 +39,7 @@ SIGNATURES = {
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
     "wan_attn_fwd_chunk": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _P]),
     "wan_attn_merge": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "wan_attn_fwd_chunk_merge": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _F, _P]),
     "wan_qkv_quant_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qknorm_rope_quant_fp8": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F,
                                                  _P, _P, _P, _P, _P]),
@@ -204,6 +206,35 @@ def attn_merge(acc_out, acc_lse, chunk_out, chunk_lse, heads, head_dim=HEAD_DIM,
         _check("wan_attn_merge", lib().wan_attn_merge(
             _ptr(acc_out), _ptr(acc_lse), _ptr(chunk_out), _ptr(chunk_lse), _ptr(out_bf16), B, Sq, heads,
             head_dim, _stream(dev, stream)))
+    return acc_out, acc_lse
+
+
+def attn_fwd_chunk_merge(q_src, kv_src, acc_out, acc_lse, heads, head_dim=HEAD_DIM, softmax_scale=None,
+                         out_bf16=None, stream=None):
+    """One ring round folded into (acc_out, acc_lse) in place: attention of
+    the queries of q_src over the chunk kv_src, merged as attn_merge would.
+    Returns (acc_out, acc_lse)."""
+    _need_gpu("q_src", q_src, torch.bfloat16)
+    _need_gpu("kv_src", kv_src, torch.bfloat16)
+    _need_gpu("acc_out", acc_out, torch.float32)
+    _need_gpu("acc_lse", acc_lse, torch.float32)
+    B, Sq, Skv = q_src.shape[0], q_src.shape[1], kv_src.shape[1]
+    D = heads * head_dim
+    if q_src.dim() != 3 or kv_src.dim() != 3 or q_src.shape[2] != 3 * D or kv_src.shape[2] != 3 * D \
+            or kv_src.shape[0] != B:
+        raise ValueError("q_src and kv_src must be [B, S, 3*heads*head_dim] with the same B")
+    if tuple(acc_out.shape) != (B, Sq, D) or tuple(acc_lse.shape) != (B, heads, Sq):
+        raise ValueError("acc_out must be [B, Sq, D] and acc_lse [B, heads, Sq]")
+    if out_bf16 is not None:
+        _need_gpu("out_bf16", out_bf16, torch.bfloat16)
+        if tuple(out_bf16.shape) != (B, Sq, D):
+            raise ValueError("out_bf16 must be [B, Sq, D]")
+    scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else float(softmax_scale)
+    dev = q_src.device
+    with torch.cuda.device(dev):
+        _check("wan_attn_fwd_chunk_merge", lib().wan_attn_fwd_chunk_merge(
+            _ptr(q_src), Sq, _ptr(kv_src), Skv, _ptr(acc_out), _ptr(acc_lse), _ptr(out_bf16), B, heads, head_dim,
+            scale, _stream(dev, stream)))
     return acc_out, acc_lse
 
 
