@@ -170,3 +170,8 @@ def test_fused_norm_quant_matches_oracle():
 def test_fused_norm_quant_720p():
     w = WORKLOADS["720p_fp8"]
     _fused_vs_two_calls(w.B, (w.T, w.H, w.W), w.heads, seed=w.seed, device_gen=True)
+
+
+def test_fused_norm_quant_beyond_one_launch():
+    """More than 2^21 token rows (several norm launches feed one amax)."""
+    _fused_vs_two_calls(1, (33, 256, 256), 1, seed=22, device_gen=True)

@@ -133,3 +133,32 @@ def _check_rows(after, ref, w, rows):
         assert ok.all(), f"{name}: {(~ok).sum()} elements outside the candidate set"
         assert exact >= 0.9999
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+
+
+def test_rows_beyond_one_launch():
+    """More than 2^21 token rows: the library splits the rows over several
+    launches; tokens on both sides of the split are checked against the
+    oracle (one head keeps the buffer at 1.7 GB)."""
+    heads, grid = 1, (33, 256, 256)
+    T, H, W = grid
+    S = T * H * W
+    assert S > 1 << 21
+    D = heads * 128
+    qkv = synth.make_qkv(1, S, heads, seed=21, device=DEV)
+    gq, gk = synth.make_gammas(D, seed=21, device=DEV)
+    rng = np.random.default_rng(21)
+    edge = (1 << 21) + np.arange(-3, 3)
+    rows = np.unique(np.concatenate([rng.integers(0, S, 1024), edge, [0, S - 1]]))
+    assert rows.min() >= 0 and rows.max() < S
+    rows_t = torch.from_numpy(rows).to(DEV)
+    host_in = _np(qkv.view(-1, 3 * D).index_select(0, rows_t))
+    wan_attn.qknorm_rope(qkv, gq, gk, grid, heads)
+    torch.cuda.synchronize()
+    after = _np(qkv.view(-1, 3 * D).index_select(0, rows_t))
+    ref = wan_ref.qknorm_rope_tokens_ref(host_in, rows % S, _np(gq), _np(gk), grid, heads, 128)
+
+    class _W:  # the fields _check_rows reads
+        pass
+    w = _W()
+    w.S, w.H, w.W, w.D, w.heads = S, H, W, D, heads
+    _check_rows(after, ref, w, rows)
