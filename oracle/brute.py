@@ -51,3 +51,17 @@ def rope_head_brute(vec, f, y, w, theta=10000.0, split=(44, 42, 42)):
         out[2 * p] = a * math.cos(phi) - b * math.sin(phi)
         out[2 * p + 1] = a * math.sin(phi) + b * math.cos(phi)
     return out
+
+
+def linear_brute(x, w, bias=None):
+    """y[m][n] = sum_k x[m][k] w[n][k] (+ bias[n]) with exact summation; lists."""
+    out = []
+    for xm in x:
+        row = []
+        for n, wn in enumerate(w):
+            terms = [xm[k] * wn[k] for k in range(len(xm))]
+            if bias is not None:
+                terms.append(bias[n])
+            row.append(math.fsum(terms))
+        out.append(row)
+    return out

@@ -251,3 +251,23 @@ def quant_fp8_ref(qkv, heads, head_dim):
         deq.append(v8 / sc)
     return {"amax": np.array(amax), "scale": np.array(scale),
             "codes": np.concatenate(codes, axis=-1), "deq": np.concatenate(deq, axis=-1)}
+
+
+def qkv_proj_ref(x, w, bias=None):
+    """The QKV projection whose output is the packed [Q|K|V] buffer.
+
+    [P5] change 1: the fused QKV projection produces Q, K and V in one shared
+    allocation; [P1] "NKI kernels": the qkv_cte kernel is this projection.
+    x    : [M, dim] float64 array (bf16 values), one token per row.
+    w    : [3 * D, dim] float64 array (bf16 values), one output feature per row
+           (features 0..D-1 are Q, D..2D-1 K, 2D..3D-1 V).
+    bias : [3 * D] float64 array (bf16 values) or None.
+    Returns (y, y16): y = x w^T + bias in fp64, and y16 = bf16(y), the value
+    stored in the packed buffer."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    y = x @ w.T
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)
+    return y, bf16_rne(y)
+
