@@ -12,7 +12,8 @@
  *     -> wan_attn_fwd    : bidirectional (unmasked) softmax attention of every
  *                          head over every token, read straight from the packed
  *                          buffer
- *   (fp8 variant: wan_qkv_quant_fp8, then wan_attn_fwd_fp8; or
+ *   (before the norm, wan_qkv_proj can fill the packed buffer from the token
+ *    activations; fp8 variant: wan_qkv_quant_fp8, then wan_attn_fwd_fp8; or
  *    wan_qknorm_rope_quant_fp8 in place of the first two steps)
  *
  * Sources (web pages on Wan2.2, cited by title and section):
@@ -83,6 +84,31 @@ int wan_abi_version(void);
 
 /* Static, human-readable text for a wan_status value. Never NULL. */
 const char *wan_status_str(int status);
+
+/*
+ * wan_qkv_proj -- the QKV projection that fills the packed buffer: for every
+ * token, [Q | K | V] = x W^T + bias. "Optimize Wan2.2 Dataflow", change 1: the
+ * fused QKV projection produces Q, K and V in one shared allocation (the
+ * buffer wan_qknorm_rope and wan_attn_fwd then read in place); "Optimizing
+ * High-Quality Offline Video Generation", NKI kernels: qkv_cte is this
+ * projection (fused there with the norm and RoPE; a norm over the full width
+ * cannot finish inside one output tile of a GEMM, so here the norm stays its
+ * own pass).
+ *
+ *   x      bf16 [B, S, D] token activations, D = heads * head_dim.
+ *   w_qkv  bf16 [3*D, D]: one row per output feature (features 0..D-1 are Q,
+ *          D..2D-1 K, 2D..3D-1 V), i.e. the stacked weights of the three
+ *          linear layers in their usual (out_features, in_features) layout.
+ *   bias   bf16 [3*D] or NULL.
+ *   qkv    bf16 [B, S, 3*D] output (the packed buffer); must not overlap an
+ *          input.
+ * Arithmetic: bf16 products accumulated in fp32 (gfx950 MFMA), bias added in
+ * fp32, one round-to-nearest-even to bf16.
+ * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN (16-byte),
+ * WAN_E_ALIAS, WAN_E_OVERFLOW, WAN_E_HIP.
+ */
+int wan_qkv_proj(const void *x, const void *w_qkv, const void *bias, void *qkv, int64_t B, int64_t S,
+                 int64_t heads, int64_t head_dim, void *stream);
 
 /*
  * wan_qknorm_rope -- in-place Q/K RMSNorm + bf16 rounding point + 3-D RoPE.

@@ -97,6 +97,16 @@ int main() {
   EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, nullptr, outb, 1, 16, 16, 2, 128, 0.088f, &z), WAN_E_NULL);
   EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, outb, 1, 16, 0, 2, 128, 0.088f, &z), WAN_E_SHAPE);
 
+  // QKV projection: x [1,16,256], w [768,256], out [1,16,768]
+  EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, outb, 1, 16, 2, 128, &z), WAN_OK);
+  EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, buf + 600000, outb, 1, 16, 2, 128, &z), WAN_OK);
+  EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, buf + 8192, 1, 16, 2, 128, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, outb + 64, outb, 1, 16, 2, 128, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_qkv_proj(buf, nullptr, nullptr, outb, 1, 16, 2, 128, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_qkv_proj(buf + 8, buf + 16384, nullptr, outb, 1, 16, 2, 128, &z), WAN_E_ALIGN);
+  EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, outb, 1, 16, 2, 64, &z), WAN_E_UNSUPPORTED);
+  EXPECT_EQ(validate_qkv_proj(nullptr, nullptr, nullptr, nullptr, 0, 16, 2, 128, &z), WAN_OK);
+
   // fp8 quantisation and attention
   alignas(16) static unsigned char qk8[1 << 16], vt8[1 << 16];
   alignas(16) static float sc[4], am[4];

@@ -1,0 +1,103 @@
+"""GPU parity of wan_qkv_proj (through the C ABI) against the fp64 oracle.
+
+The GPU accumulates bf16 products in fp32 (MFMA) and rounds once to bf16, so
+each output must equal the bf16 rounding of some value within the fp32
+accumulation error of the exact result: |err| <= 2^-16 * sum_k |x_k w_k| (a
+generous bound on 5120-term fp32 sums), i.e. a value between
+bf16(exact - E) and bf16(exact + E); at least 99% must equal bf16(exact).
+Small shapes are compared in full (ragged token and feature tiles included),
+the full 480p shape on sampled tokens against every feature.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import wan_ref
+from oracle.numerics import bf16_rne
+from video_diffusion_transformer_amd import synth, wan_attn
+from video_diffusion_transformer_amd.configs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _check(gpu, x, w, b, what):
+    y, y16 = wan_ref.qkv_proj_ref(x, w, b)
+    E = 2.0 ** -16 * (np.abs(x) @ np.abs(w).T) + (0.0 if b is None else 2.0 ** -24 * np.abs(b))
+    lo, hi = bf16_rne(y - E), bf16_rne(y + E)
+    ok = (gpu >= lo) & (gpu <= hi)
+    assert ok.all(), f"{what}: {(~ok).sum()} outputs outside the accumulation window"
+    exact = np.mean(gpu == y16)
+    assert exact >= 0.99, f"{what}: only {exact:.4f} equal bf16(exact)"
+    return exact
+
+
+@pytest.mark.parametrize("B,S,heads,with_bias", [(1, 1, 1, True), (1, 77, 2, False), (2, 300, 2, True),
+                                                 (1, 513, 3, True), (1, 256, 1, False)])
+def test_small_full(B, S, heads, with_bias):
+    D = heads * 128
+    x = synth.make_tokens(B, S, D, seed=S + heads)
+    w, b = synth.make_qkv_weights(D, seed=S + heads)
+    b = b if with_bias else None
+    out = wan_attn.qkv_proj(x.to(DEV), w.to(DEV), heads, bias=None if b is None else b.to(DEV))
+    torch.cuda.synchronize()
+    _check(_np(out).reshape(B * S, 3 * D), _np(x).reshape(B * S, D), _np(w), None if b is None else _np(b),
+           f"B{B} S{S} h{heads}")
+
+
+def test_480p_sampled_tokens():
+    """Full 480p shape (65,520 tokens x 5120 -> 15360) in the configuration the
+    benchmark times; 96 seeded tokens plus the first and last token and the
+    edges of the last token tile, against every output feature."""
+    w480 = WORKLOADS["480p"]
+    B, S, heads, D = w480.B, w480.S, w480.heads, w480.D
+    x = synth.make_tokens(B, S, D, seed=w480.seed, device=DEV)
+    w, b = synth.make_qkv_weights(D, seed=w480.seed, device=DEV)
+    out = wan_attn.qkv_proj(x, w, heads, bias=b)
+    torch.cuda.synchronize()
+    M = B * S
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 96), [0, M - 1, (M // 256) * 256, (M // 256) * 256 - 1]]))
+    assert rows.min() >= 0 and rows.max() < M
+    rt = torch.from_numpy(rows).to(DEV)
+    g = _np(out.view(M, 3 * D).index_select(0, rt))
+    xs = _np(x.view(M, D).index_select(0, rt))
+    _check(g, xs, _np(w), _np(b), "480p")
+
+
+def test_projection_feeds_the_step():
+    """qkv_proj output is the packed buffer the norm + RoPE and attention read:
+    chained on the GPU it matches the oracle chain on the same bf16 buffer."""
+    heads, grid = 2, (2, 8, 8)
+    S, D = 128, 256
+    x = synth.make_tokens(1, S, D, seed=3)
+    w, b = synth.make_qkv_weights(D, seed=3)
+    qkv = wan_attn.qkv_proj(x.to(DEV), w.to(DEV), heads, bias=b.to(DEV))
+    torch.cuda.synchronize()
+    _, y16 = wan_ref.qkv_proj_ref(_np(x).reshape(S, D), _np(w), _np(b))
+    g = _np(qkv).reshape(S, 3 * D)
+    assert np.mean(g == y16) >= 0.99
+    gq, gk = synth.make_gammas(D, seed=3, device=DEV)
+    wan_attn.qknorm_rope(qkv, gq, gk, grid, heads)
+    out = wan_attn.attn_fwd(qkv, heads)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+
+
+def test_errors():
+    x = torch.zeros((1, 8, 256), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((768, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        wan_attn.qkv_proj(x, w[:512], 2)
+    out = torch.empty((1, 8, 768), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(wan_attn.WanError) as e:  # output on top of the weights
+        wan_attn.qkv_proj(x, w, 2, out=w.view(-1)[:8 * 768].view(1, 8, 768))
+    assert e.value.status == -5
+    assert wan_attn.qkv_proj(x[:, :0], w, 2).shape == (1, 0, 768)
+    del out

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwan_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "qknorm_rope.hip", "attn_fwd.hip", "attn_merge.hip", "quant_fp8.hip", "attn_fwd_fp8.hip"]
+SOURCES = ["api.cpp", "qkv_proj.hip", "qknorm_rope.hip", "attn_fwd.hip", "attn_merge.hip", "quant_fp8.hip",
+           "attn_fwd_fp8.hip"]
 
 
 def hipcc():

@@ -84,6 +84,17 @@ const char* wan_status_str(int status) {
   }
 }
 
+int wan_qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t B, int64_t S, int64_t heads,
+                 int64_t head_dim, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_qkv_proj(x, w_qkv, bias, qkv, B, S, heads, head_dim, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (wan::launch_qkv_proj(x, w_qkv, bias, qkv, z.rows, static_cast<int>(3 * z.D), static_cast<int>(z.D),
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
 int wan_qknorm_rope(void* qkv, const void* gamma_q, const void* gamma_k, int64_t B, int64_t T,
                     int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
                     void* stream) {

@@ -41,6 +41,11 @@ hipError_t launch_amax_clear(float* amax, hipStream_t stream);
 hipError_t launch_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, const float* amax, int B, int S,
                             int heads, hipStream_t stream);
 
+// QKV projection out[M, N] = x[M, K] w[N, K]^T (+ bias), bf16; K a multiple of
+// 64, N a multiple of 4.
+hipError_t launch_qkv_proj(const void* x, const void* w, const void* bias, void* out, int64_t M, int N, int K,
+                           hipStream_t stream);
+
 // fp8 attention forward from the quantised buffers.
 hipError_t launch_attn_fwd_fp8(const void* qk8, const void* vt8, const float* scales, void* out, float* lse, int B,
                                int S, int heads, float softmax_scale, hipStream_t stream);

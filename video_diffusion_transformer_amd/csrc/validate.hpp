@@ -160,6 +160,21 @@ inline int validate_attn_chunk_fold(const void* q_src, const void* kv_src, const
   return WAN_OK;
 }
 
+// QKV projection: x [B, S, D], w [3D, D], bias [3D] (optional), out [B, S, 3D];
+// out must not overlap an input.
+inline int validate_qkv_proj(const void* x, const void* w, const void* bias, const void* out, int64_t B, int64_t S,
+                             int64_t heads, int64_t head_dim, Sizes* z) {
+  int rc = check_sizes(B, S, heads, head_dim, z);
+  if (rc != WAN_OK || z->empty) return rc;
+  if (!x || !w || !out) return WAN_E_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16) || (bias && !aligned(bias, 16))) return WAN_E_ALIGN;
+  const int64_t x_bytes = z->out_elems * 2, w_bytes = 3 * z->D * z->D * 2, b_bytes = 3 * z->D * 2,
+                o_bytes = z->qkv_elems * 2;
+  if (overlaps(out, o_bytes, x, x_bytes) || overlaps(out, o_bytes, w, w_bytes) || overlaps(out, o_bytes, bias, b_bytes))
+    return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 // Bytes of the transposed fp8 V buffer: B * heads * 128 * S_pad, S_pad = S rounded up to 128.
 inline bool fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t* out) {
   const int64_t s_pad = (S + 127) / 128 * 128;

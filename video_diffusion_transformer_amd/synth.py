@@ -1,10 +1,11 @@
 """Seeded synthetic inputs for the self-attention step.
 
 This module holds no arithmetic of the method: it only draws the packed QKV
-activations (independent N(0, 1) values rounded to bfloat16) and the two RMSNorm
-weight vectors (1 + 0.1 * N(0, 1), rounded to bfloat16), from a torch generator
-seeded per workload. Both the HIP path and the CPU oracle receive exactly these
-tensors.
+activations (independent N(0, 1) values rounded to bfloat16), the two RMSNorm
+weight vectors (1 + 0.1 * N(0, 1), rounded to bfloat16), and, for the QKV
+projection, token activations (N(0, 1)) and a weight matrix and bias
+(N(0, 1/dim) and 0.02 N(0, 1)), from torch generators seeded per workload. Both
+the HIP path and the CPU oracle receive exactly these tensors.
 
 The pages measure on the MLPerf Wan2.2 720p workload, whose activations are not
 available; these draws stand in for it with the same shapes. Dense attention
@@ -41,3 +42,27 @@ def make_gammas(D, seed=0, device="cpu"):
     g = 1.0 + 0.1 * torch.randn((2, D), generator=gen, dtype=torch.float32)
     g = g.to(torch.bfloat16).to(device)
     return g[0].contiguous(), g[1].contiguous()
+
+
+def make_tokens(B, S, dim, seed=0, device="cpu", chunk_tokens=8192):
+    """Token activations [B, S, dim] bfloat16 of N(0, 1) draws (chunked like make_qkv)."""
+    out = torch.empty((B, S, dim), dtype=torch.bfloat16, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(20_000 + seed)
+    flat = out.view(B * S, dim)
+    for i in range(0, B * S, chunk_tokens):
+        n = min(chunk_tokens, B * S - i)
+        flat[i:i + n] = torch.randn((n, dim), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
+def make_qkv_weights(dim, seed=0, device="cpu"):
+    """Stacked QKV projection weights [3 * dim, dim] bfloat16 = bf16(N(0, 1/dim))
+    (unit-variance outputs for unit-variance inputs) and the bias [3 * dim] =
+    bf16(0.02 N(0, 1)), drawn on the CPU so they do not depend on the device."""
+    gen = torch.Generator()
+    gen.manual_seed(30_000 + seed)
+    w = (torch.randn((3 * dim, dim), generator=gen, dtype=torch.float32) * dim ** -0.5).to(torch.bfloat16)
+    b = (0.02 * torch.randn((3 * dim,), generator=gen, dtype=torch.float32)).to(torch.bfloat16)
+    return w.to(device), b.to(device)
+

@@ -5,7 +5,7 @@ kernels behind the C ABI declared in include/wan_attn.h. Tensors must already
 live on the GPU; there is no CPU path. If the library is not built the first
 call raises -- nothing falls back to another implementation.
 
-The names follow the C ABI: ``qknorm_rope`` -> wan_qknorm_rope,
+The names follow the C ABI: ``qkv_proj`` -> wan_qkv_proj, ``qknorm_rope`` -> wan_qknorm_rope,
 ``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_chunk`` -> wan_attn_fwd_chunk,
 ``attn_merge`` -> wan_attn_merge, ``attn_fwd_chunk_merge`` -> wan_attn_fwd_chunk_merge,
 ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
@@ -35,6 +35,7 @@ _P, _I64, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
 SIGNATURES = {
     "wan_abi_version": (ctypes.c_int, []),
     "wan_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "wan_qkv_proj": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
     "wan_attn_fwd_chunk": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _P]),
@@ -106,6 +107,29 @@ def token_grid(width, height, num_frames):
     w = (width // 16) * 16 // 8 // 2
     h = (height // 16) * 16 // 8 // 2
     return (num_frames - 1) // 4 + 1, h, w
+
+
+def qkv_proj(x, w_qkv, heads, bias=None, head_dim=HEAD_DIM, out=None, stream=None):
+    """Packed [B, S, 3D] bf16 = x [B, S, D] w_qkv^T (+ bias), w_qkv [3D, D].
+    Returns the output tensor (allocated unless ``out`` is given)."""
+    D = heads * head_dim
+    _need_gpu("x", x, torch.bfloat16)
+    _need_gpu("w_qkv", w_qkv, torch.bfloat16)
+    if bias is not None:
+        _need_gpu("bias", bias, torch.bfloat16)
+        if bias.numel() != 3 * D:
+            raise ValueError("bias must have 3*heads*head_dim elements")
+    if x.dim() != 3 or x.shape[2] != D or tuple(w_qkv.shape) != (3 * D, D):
+        raise ValueError("x must be [B, S, heads*head_dim] and w_qkv [3*D, D]")
+    B, S = x.shape[0], x.shape[1]
+    out = torch.empty((B, S, 3 * D), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need_gpu("out", out, torch.bfloat16)
+    if tuple(out.shape) != (B, S, 3 * D):
+        raise ValueError("out must be [B, S, 3*D]")
+    with torch.cuda.device(x.device):
+        _check("wan_qkv_proj", lib().wan_qkv_proj(
+            _ptr(x), _ptr(w_qkv), _ptr(bias), _ptr(out), B, S, heads, head_dim, _stream(x.device, stream)))
+    return out
 
 
 def qknorm_rope(qkv, gamma_q, gamma_k, grid, heads, head_dim=HEAD_DIM, eps=RMS_EPS,
