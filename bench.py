@@ -23,6 +23,10 @@ line is printed.
               sequence split over --ring-cp ranks: S/cp queries against cp
               K/V chunks, each round folded into the accumulator by the
               log-sum-exp merge; not part of the step or of value.
+  qkv_proj    (bf16 workloads) the QKV projection x W^T + b that produces the
+              packed [Q|K|V] buffer the step reads: FLOP per launch over the
+              launch time from HIP events on its stream, against the bf16
+              MFMA peak; not part of the step or of value.
 """
 
 import argparse
@@ -39,7 +43,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "attn_fwd_fp8": "attn_fwd_fp8.hip",
-                  "qknorm_rope": "qknorm_rope.hip"}
+                  "qknorm_rope": "qknorm_rope.hip", "qkv_proj": "qkv_proj.hip"}
 
 
 def kernel_source_hash(name):
@@ -145,6 +149,37 @@ def ring_share(w, qkv, cp, reps=3):
                     "epilogue; TFLOP/s counts the attention FLOP of the share over the whole share time"}
 
 
+def qkv_proj(w, dev, reps=3):
+    """The QKV projection on the workload's token matrix: x [B, S, D] times the
+    fused weight [3D, D] plus bias into the packed [B, S, 3D] buffer. One
+    warm-up call, then reps calls timed with HIP events on the stream."""
+    import torch
+
+    from video_diffusion_transformer_amd import synth, wan_attn
+
+    if reps < 1 or w.dtype != "bf16":
+        return None
+    x = synth.make_tokens(w.B, w.S, w.D, seed=w.seed, device=dev)
+    wq, bq = synth.make_qkv_weights(w.D, seed=w.seed, device=dev)
+    out = torch.empty((w.B, w.S, 3 * w.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    wan_attn.qkv_proj(x, wq, w.heads, bias=bq, out=out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        wan_attn.qkv_proj(x, wq, w.heads, bias=bq, out=out)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    flop = 2.0 * w.B * w.S * 3 * w.D * w.D
+    tf = flop / (ms * 1e-3) / 1e12
+    del x, wq, bq, out
+    return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_TFLOPS["bf16"], 4), "ms_per_launch": round(ms, 4), "flop_per_launch": flop,
+            "traffic": committed_traffic("qkv_proj", w.name)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +193,8 @@ def main():
     ap.add_argument("--ring-cp", type=int, default=8, metavar="CP",
                     help="also time one GPU's share of ring attention with the sequence split over CP ranks "
                          "(bf16 workloads; 0 to skip)")
+    ap.add_argument("--proj-reps", type=int, default=3, metavar="N",
+                    help="timed calls of the QKV projection on the workload's tokens (bf16 workloads; 0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, run one plain device copy of MIB MiB (its hardware "
                          "counters scale FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -272,6 +309,9 @@ def main():
         ring = ring_share(w, qkv, args.ring_cp)
         if ring:
             rec["ring_share"] = ring
+    proj = qkv_proj(w, dev, args.proj_reps)
+    if proj:
+        rec["qkv_proj"] = proj
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
