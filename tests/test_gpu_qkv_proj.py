@@ -6,8 +6,10 @@ accumulation error of the exact result: |err| <= 2^-16 * sum_k |x_k w_k| (a
 generous bound on 5120-term fp32 sums), i.e. a value between
 bf16(exact - E) and bf16(exact + E); at least 99% must equal bf16(exact).
 Small shapes are compared in full (ragged token and feature tiles included),
-the full 480p shape on sampled tokens against every feature.
+the full 480p and 720p shapes on sampled tokens against every feature.
 """
+
+import math
 
 import numpy as np
 import pytest
@@ -15,6 +17,7 @@ import torch
 
 from oracle import wan_ref
 from oracle.numerics import bf16_rne
+from tests.parity import BF16_GATES, LSE_ABS, assert_gates, attn_error_stats
 from video_diffusion_transformer_amd import synth, wan_attn
 from video_diffusion_transformer_amd.configs import WORKLOADS
 
@@ -51,14 +54,16 @@ def test_small_full(B, S, heads, with_bias):
            f"B{B} S{S} h{heads}")
 
 
-def test_480p_sampled_tokens():
-    """Full 480p shape (65,520 tokens x 5120 -> 15360) in the configuration the
-    benchmark times; 96 seeded tokens plus the first and last token and the
-    edges of the last token tile, against every output feature."""
-    w480 = WORKLOADS["480p"]
-    B, S, heads, D = w480.B, w480.S, w480.heads, w480.D
-    x = synth.make_tokens(B, S, D, seed=w480.seed, device=DEV)
-    w, b = synth.make_qkv_weights(D, seed=w480.seed, device=DEV)
+@pytest.mark.parametrize("name", ["480p", "720p"])
+def test_full_size_sampled_tokens(name):
+    """Full workload shape (480p: 65,520 tokens, 720p: 151,200 tokens, x 5120
+    -> 15360) in the configuration the benchmark times; 96 seeded tokens plus
+    the first and last token and the edges of the last token tile, against
+    every output feature."""
+    wl = WORKLOADS[name]
+    B, S, heads, D = wl.B, wl.S, wl.heads, wl.D
+    x = synth.make_tokens(B, S, D, seed=wl.seed, device=DEV)
+    w, b = synth.make_qkv_weights(D, seed=wl.seed, device=DEV)
     out = wan_attn.qkv_proj(x, w, heads, bias=b)
     torch.cuda.synchronize()
     M = B * S
@@ -68,26 +73,34 @@ def test_480p_sampled_tokens():
     rt = torch.from_numpy(rows).to(DEV)
     g = _np(out.view(M, 3 * D).index_select(0, rt))
     xs = _np(x.view(M, D).index_select(0, rt))
-    _check(g, xs, _np(w), _np(b), "480p")
+    _check(g, xs, _np(w), _np(b), name)
 
 
 def test_projection_feeds_the_step():
     """qkv_proj output is the packed buffer the norm + RoPE and attention read:
-    chained on the GPU it matches the oracle chain on the same bf16 buffer."""
+    the GPU chain (projection, norm + RoPE in place, attention) against the
+    oracle chain from the same x, W, b (the oracle's own bf16 projection feeds
+    its norm and attention), to the bf16 attention gates."""
     heads, grid = 2, (2, 8, 8)
     S, D = 128, 256
     x = synth.make_tokens(1, S, D, seed=3)
     w, b = synth.make_qkv_weights(D, seed=3)
+    gq, gk = synth.make_gammas(D, seed=3)
     qkv = wan_attn.qkv_proj(x.to(DEV), w.to(DEV), heads, bias=b.to(DEV))
     torch.cuda.synchronize()
     _, y16 = wan_ref.qkv_proj_ref(_np(x).reshape(S, D), _np(w), _np(b))
-    g = _np(qkv).reshape(S, 3 * D)
-    assert np.mean(g == y16) >= 0.99
-    gq, gk = synth.make_gammas(D, seed=3, device=DEV)
-    wan_attn.qknorm_rope(qkv, gq, gk, grid, heads)
-    out = wan_attn.attn_fwd(qkv, heads)
+    assert np.mean(_np(qkv).reshape(S, 3 * D) == y16) >= 0.99
+    wan_attn.qknorm_rope(qkv, gq.to(DEV), gk.to(DEV), grid, heads)
+    out, lse = wan_attn.attn_fwd(qkv, heads, lse=True)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
+    host = y16.reshape(1, S, 3 * D)
+    r = wan_ref.qknorm_rope_ref(host, _np(gq), _np(gk), grid, heads, 128)
+    normed = host.copy().reshape(S, 3 * D)
+    normed[:, :D] = r["out16_q"]
+    normed[:, D:2 * D] = r["out16_k"]
+    o_ref, l_ref = wan_ref.attn_packed_ref(normed.reshape(1, S, 3 * D), heads, 128, 1.0 / math.sqrt(128.0))
+    assert_gates(attn_error_stats(_np(out), o_ref), BF16_GATES, "projection chain")
+    assert np.abs(_np(lse) - l_ref).max() <= LSE_ABS
 
 
 def test_errors():
