@@ -6,23 +6,27 @@
 //
 // Design (gfx950):
 //   * workgroup = 8 waves, output tile 256 tokens x 256 features, K in steps of
-//     64 through a ring of LDS stages (by default two of 64 KB), filled straight
-//     from global memory by buffer_load_dwordx4 ... lds (no staging
-//     registers). The buffer form takes one descriptor per operand tile and a
-//     32-bit offset per lane, and rows past the end of the matrix read as
-//     zeros. (The global_load_lds form of the same copy measured slower: its
-//     requests queue behind the LDS commands of the fragment reads.)
+//     64 through two LDS stages of 64 KB, filled straight from global memory
+//     by buffer_load_dwordx4 ... lds (no staging registers). The buffer form
+//     takes one descriptor per operand tile and a 32-bit offset per lane, and
+//     rows past the end of the matrix read as zeros. (The global_load_lds form
+//     of the same copy measured slower: its requests queue behind the LDS
+//     commands of the fragment reads.)
 //   * the tile is computed transposed, C^T = W X^T (A = 16 features x 32
 //     channels of W, B = 32 channels x 16 tokens of x), so each lane ends with 4
 //     consecutive features of one token;
 //   * waves are 2 (features) x 4 (tokens), each owning 128 x 64 outputs = 32
-//     MFMA tiles; per 32-channel step a wave reads 8 W and 4 x fragments (16 B
-//     per lane) and issues 32 MFMAs;
+//     MFMA tiles; per 32-channel half step a wave reads 8 W and 4 x fragments
+//     (16 B per lane) and issues 32 MFMAs;
+//   * the copies of the next step are spread over the first half's MFMAs, one
+//     per two MFMAs: issued in one burst, the copies of all waves fill the
+//     texture unit's queues and the in-order wave stalls with its MFMAs behind
+//     them (+5%);
 //   * 128-byte LDS rows (64 channels) with the 16-byte chunk XOR-swizzled by
-//     the row (see p_swz): conflict-free fragment reads;
+//     the row (p_swz): conflict-free fragment reads;
 //   * epilogue through LDS: the tile is written to LDS and stored as whole
 //     256-byte row segments (8-byte stores straight from the MFMA layout touch
-//     16 rows per instruction and stall the texture unit's write path: +6%);
+//     16 rows per store and stall the texture unit's write path: +6%);
 //   * workgroups are numbered XCD-major and then in groups of 8 token tiles
 //     sweeping the feature tiles, so the ~32 workgroups an XCD runs at once
 //     share 8 x tiles and 4 W tiles in its L2 (groups of 16 or 32 token tiles
@@ -34,45 +38,23 @@ namespace wan {
 
 namespace {
 
-#ifndef WAN_PROJ_BK
-#define WAN_PROJ_BK 64
-#endif
-#ifndef WAN_PROJ_STAGES
-#define WAN_PROJ_STAGES 2
-#endif
-constexpr int kPM = 256, kPN = 256, kPK = WAN_PROJ_BK;  // tile: tokens, features, channels per step
-constexpr int kPStages = WAN_PROJ_STAGES;               // LDS stages; kPStages - 1 steps in flight
+constexpr int kPM = 256, kPN = 256, kPK = 64;  // tile: tokens, features, channels per step
 constexpr int kPWaves = 8, kPThreads = 64 * kPWaves;
 constexpr int kPRow = kPK * 2;                 // bytes per LDS row
-constexpr int kPChunks = kPRow / 16;           // 16-byte chunks per row
-constexpr int kPTile = kPM * kPRow;            // bytes per operand tile
+constexpr int kPTile = kPM * kPRow;            // 32 KB per operand tile
 constexpr int kPStage = 2 * kPTile;            // W tile + x tile
-#ifndef WAN_PROJ_GROUP
-#define WAN_PROJ_GROUP 8
-#endif
-constexpr int kPGroup = WAN_PROJ_GROUP;        // token tiles per ordering group
-constexpr int kPBlk = kPTile / 1024 / kPWaves;  // 1 KB blocks per wave per operand tile
-constexpr int kPRowsPerBlk = 1024 / kPRow;
-constexpr int kPLoads = 2 * kPBlk;             // loads per wave per step
-constexpr int kPSub = kPK / 32;                // 32-channel MFMA steps per K step
+constexpr int kPGroup = 8;                     // token tiles per ordering group
+constexpr int kPBlk = kPTile / 1024 / kPWaves;  // 1 KB blocks (8 rows) per wave per operand tile (4)
+constexpr int kPLoads = 2 * kPBlk;             // copies per wave per step (8)
 static_assert(kPM == kPN, "one staging layout serves both operands");
-static_assert(kPK == 32 || kPK == 64, "one or two 32-channel MFMA steps per K step");
-static_assert(kPStages >= 2 && kPStages * kPStage <= 160 * 1024, "stages must fit the 160 KB of LDS");
-static_assert(kPWaves * 64 * 256 <= kPStages * kPStage, "the epilogue needs 16 KB per wave");
-// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt unconstrained
-constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
-static_assert((kPStages - 2) * kPLoads < 64, "vmcnt is 6 bits");
+static_assert(kPWaves * 64 * 256 <= 2 * kPStage, "the epilogue needs 16 KB per wave");
+constexpr int kWaitVm0 = 0x0f70;               // s_waitcnt vmcnt(0), other counters unconstrained
 
-// XOR swizzle of the 16-byte chunk by the row. 8 chunks (128-byte rows):
-// r1 | r2 << 1 | (r0 ^ r3) << 2; 4 chunks (64-byte rows): r2 | (r1 ^ r3) << 1.
-// Either way each half-wave's 32 fragment reads land on 32 distinct 16-byte
-// slots of a 512-byte window (and every 8 or 16 consecutive lanes on distinct
-// slots of 128 or 256 bytes), which the gfx950 LDS serves without bank
-// conflicts.
-__device__ __forceinline__ int p_swz(int r) {
-  if constexpr (kPChunks == 8) return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2);
-  else return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
-}
+// XOR swizzle of the 16-byte chunk of a 128-byte row: r1 | r2 << 1 | (r0 ^ r3)
+// << 2. Each half-wave's 32 fragment reads land on 32 distinct 16-byte slots
+// of a 512-byte window (and every 8 or 16 consecutive lanes on distinct slots
+// of 128 or 256 bytes), which the gfx950 LDS serves without bank conflicts.
+__device__ __forceinline__ int p_swz(int r) { return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2); }
 
 __device__ __forceinline__ int p_xcd_remap(int bid, int nb) {
   const int xcd = bid & 7, j = bid >> 3;
@@ -89,7 +71,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __global__ void __launch_bounds__(kPThreads, 1)
 qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
                 uint16_t* __restrict__ out, int M, int N, int K, int ntm, int ntn) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kPStages * kPStage];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kPStage];
 
   // Tile order: XCD-major, then groups of kPGroup token tiles x all feature tiles.
   const int lid = p_xcd_remap(blockIdx.x, gridDim.x);
@@ -108,9 +90,9 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
 
   // Staging: each wave fills kPBlk 1 KB blocks (8 rows of 128 B) of the W tile
   // and of the x tile; lane l of a block takes physical row 8 blk + l/8,
-  // physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row).
-  // One buffer descriptor per operand tile, sized to the rows that exist: rows
-  // past N or M read as zeros (and are never stored).
+  // physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row). One buffer
+  // descriptor per operand tile, sized to the rows that exist: rows past N or
+  // M read as zeros (and are never stored).
   const uint32_t wbytes = (uint32_t)(min(N - n0, kPN) * K * 2), xbytes = (uint32_t)(min(M - m0, kPM) * K * 2);
   const __amdgpu_buffer_rsrc_t wrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w + (int64_t)n0 * K), (short)0, (int)wbytes, 0x00020000);
@@ -119,8 +101,8 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
   uint32_t goff[kPBlk];
 #pragma unroll
   for (int j = 0; j < kPBlk; ++j) {
-    const int r = kPRowsPerBlk * (kPBlk * wave + j) + lane / kPChunks;
-    goff[j] = (uint32_t)(r * K * 2 + 16 * ((lane % kPChunks) ^ p_swz(r)));
+    const int r = 8 * (kPBlk * wave + j) + (lane >> 3);
+    goff[j] = (uint32_t)(r * K * 2 + 16 * ((lane & 7) ^ p_swz(r)));
   }
   auto issue = [&](int kt, int stage) {
     unsigned char* dst = smem + stage * kPStage + kPBlk * wave * 1024;
@@ -133,10 +115,10 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
 
   // Fragment reads: lane (l16, grp) reads row 16 t + l16 at logical chunk 4 s +
   // grp; the swizzle depends on the row only through l16, so the per-lane byte
-  // offset of a read is fixed for each 32-channel sub-step s.
-  int roff[kPSub];
+  // offset of a read is fixed for each 32-channel half s.
+  int roff[2];
 #pragma unroll
-  for (int s = 0; s < kPSub; ++s) roff[s] = l16 * kPRow + 16 * ((4 * s + grp) ^ p_swz(l16));
+  for (int s = 0; s < 2; ++s) roff[s] = l16 * kPRow + 16 * ((4 * s + grp) ^ p_swz(l16));
 
   f32x4_t acc[8][4];
 #pragma unroll
@@ -144,44 +126,56 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{};
 
-  // Ring of kPStages stages: step kt lives in stage kt % kPStages, and the
-  // loads of step kt + kPStages - 1 go into the stage of step kt - 1, which
-  // every wave finished reading before the barrier that opens iteration kt.
+  // Step kt lives in stage kt & 1. Iteration kt copies step kt + 1 (past the
+  // last step: the last step again, into the stage nobody reads any more), so
+  // the loop body is one basic block the schedule below can arrange.
   const int nk = K / kPK;
-#pragma unroll
-  for (int p = 0; p < kPStages - 1; ++p)
-    if (p < nk) issue(p, p);
-  int rd = 0, wr = kPStages - 1;
+  issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    // This wave's loads of step kt have landed (those of later steps may still
-    // be in flight; near the end all are waited for) ...
-    if (kt + kPStages - 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm((kPStages - 2) * kPLoads));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // ... and, past the barrier, every wave's. A bare barrier: the fence of
-    // __syncthreads() would also wait for the loads of the later steps.
+    // This wave's copies of step kt have landed; past the barrier, every
+    // wave's, and every wave has finished reading step kt - 1, whose stage is
+    // refilled below. A bare barrier: the fence of __syncthreads() adds nothing
+    // the explicit wait does not.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     asm volatile("s_barrier" ::: "memory");
-    if (kt + kPStages - 1 < nk) issue(kt + kPStages - 1, wr);
-    const unsigned char* st = smem + rd * kPStage;
-#pragma unroll
-    for (int s = 0; s < kPSub; ++s) {
-      bf16x8_t a[8], b[4];
+    const unsigned char* st = smem + (kt & 1) * kPStage;
+    bf16x8_t a[2][8], b[2][4];
+    auto read = [&](int s) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(st + (128 * wn + 16 * i) * kPRow + roff[s]);
+        a[s][i] = *reinterpret_cast<const bf16x8_t*>(st + (128 * wn + 16 * i) * kPRow + roff[s]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(st + kPTile + (64 * wm + 16 * j) * kPRow + roff[s]);
+        b[s][j] = *reinterpret_cast<const bf16x8_t*>(st + kPTile + (64 * wm + 16 * j) * kPRow + roff[s]);
+    };
+    auto mfmas = [&](int s) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[s][i], b[s][j], acc[i][j]);
+    };
+    // The copies follow the first half's fragment reads in program order (the
+    // compiler cannot tell the stages apart and keeps LDS reads and LDS-writing
+    // copies in order) and interleave with its MFMAs; the second half's reads
+    // follow the copies.
+    read(0);
+    issue(min(kt + 1, nk - 1), (kt + 1) & 1);
+    mfmas(0);
+    read(1);
+    mfmas(1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // 12 fragment reads
+#pragma unroll
+    for (int q = 0; q < kPLoads; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // 1 copy
     }
-    rd = rd + 1 == kPStages ? 0 : rd + 1;
-    wr = wr + 1 == kPStages ? 0 : wr + 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 64 - 2 * kPLoads, 0);
+    __builtin_amdgcn_sched_barrier(0);  // nothing moves past the next iteration's wait
   }
-  // Every wave has finished its MFMAs' LDS reads before the epilogue reuses
-  // the stages.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // The last copies (a reload) land, and every wave leaves the stages, before
+  // the epilogue reuses the LDS.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 
   // Epilogue through LDS (free after the last barrier): each wave writes its
