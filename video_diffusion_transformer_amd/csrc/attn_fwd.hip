@@ -15,7 +15,7 @@
 //     serves 384 queries;
 //   * keys stream in tiles of 64 through two LDS stages, filled straight from
 //     global memory by buffer_load_dwordx4 ... lds (no staging registers): tile j+1
-//     is requested at the top of the iteration that consumes tile j, and one
+//     is requested during the score MFMAs of the iteration that consumes tile j, and one
 //     wait + barrier per tile publishes it;
 //   * scores are computed transposed, S^T = K Q^T (16x16x32 MFMA: A = 16 keys x
 //     32 channels from LDS, B = Q held in registers), so after the MFMA each
@@ -336,9 +336,18 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
   __syncthreads();
   for (int kt = 0; kt < a.nkt; ++kt) {
     const int cur = (kt & 1) * kStage;
-    // The other stage was last read in iteration kt-1, which every wave has left.
-    if (kt + 1 < a.nkt) issue_tile(a, kt * kBN + kBN, smem, ((kt + 1) & 1) * kStage);
+    // The copies of tile kt+1 (past the last tile: the last tile again, into
+    // the stage nobody reads any more) go into the other stage, last read in
+    // iteration kt-1, which every wave has left. They follow the score
+    // fragment reads in program order and are spread over the score MFMAs, one
+    // per 8 (+1% over issuing them in one burst at the top).
     tile_scores(a, smem, cur, qf, acc_s);
+    issue_tile(a, min(kt + 1, a.nkt - 1) * kBN, smem, ((kt + 1) & 1) * kStage);
+#pragma unroll
+    for (int q = 0; q < 2 * kBlk; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // 1 copy
+    }
     const unsigned moved = tile_max(a, kt * kBN, acc_s, m_run, acc_l, alpha);
     if (moved) tile_rescale(moved, alpha, acc_o);
     tile_exp(a, acc_s, m_run, pf, acc_l);
