@@ -105,7 +105,8 @@ const char *wan_status_str(int status);
  * Arithmetic: bf16 products accumulated in fp32 (gfx950 MFMA), bias added in
  * fp32, one round-to-nearest-even to bf16.
  * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN (16-byte),
- * WAN_E_ALIAS, WAN_E_OVERFLOW, WAN_E_HIP.
+ * WAN_E_ALIAS, WAN_E_OVERFLOW (also B*S above 2^31 - 257 token rows),
+ * WAN_E_HIP.
  */
 int wan_qkv_proj(const void *x, const void *w_qkv, const void *bias, void *qkv, int64_t B, int64_t S,
                  int64_t heads, int64_t head_dim, void *stream);

@@ -106,6 +106,9 @@ int main() {
   EXPECT_EQ(validate_qkv_proj(buf + 8, buf + 16384, nullptr, outb, 1, 16, 2, 128, &z), WAN_E_ALIGN);
   EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, outb, 1, 16, 2, 64, &z), WAN_E_UNSUPPORTED);
   EXPECT_EQ(validate_qkv_proj(nullptr, nullptr, nullptr, nullptr, 0, 16, 2, 128, &z), WAN_OK);
+  // B * S token rows past 2^31 - 257 do not fit the GEMM's 32-bit row indices
+  EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, outb, 2, 1 << 30, 2, 128, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, outb, 1, (1LL << 31) - 300, 2, 128, &z), WAN_E_ALIAS);
 
   // fp8 quantisation and attention
   alignas(16) static unsigned char qk8[1 << 16], vt8[1 << 16];

@@ -166,6 +166,7 @@ inline int validate_qkv_proj(const void* x, const void* w, const void* bias, con
                              int64_t heads, int64_t head_dim, Sizes* z) {
   int rc = check_sizes(B, S, heads, head_dim, z);
   if (rc != WAN_OK || z->empty) return rc;
+  if (z->rows > kMaxTokens - 256) return WAN_E_OVERFLOW;  // token rows and tile offsets are 32-bit in the GEMM
   if (!x || !w || !out) return WAN_E_NULL;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16) || (bias && !aligned(bias, 16))) return WAN_E_ALIGN;
   const int64_t x_bytes = z->out_elems * 2, w_bytes = 3 * z->D * z->D * 2, b_bytes = 3 * z->D * 2,
