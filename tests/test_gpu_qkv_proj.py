@@ -103,6 +103,32 @@ def test_projection_feeds_the_step():
     assert np.abs(_np(lse) - l_ref).max() <= LSE_ABS
 
 
+def test_wide_model():
+    """64 heads (D = 8192: 128 K steps, 96 feature tiles) on a few tokens,
+    every output against the oracle."""
+    heads, S = 64, 5
+    D = heads * 128
+    x = synth.make_tokens(1, S, D, seed=64)
+    w, b = synth.make_qkv_weights(D, seed=64)
+    out = wan_attn.qkv_proj(x.to(DEV), w.to(DEV), heads, bias=b.to(DEV))
+    torch.cuda.synchronize()
+    _check(_np(out).reshape(S, 3 * D), _np(x).reshape(S, D), _np(w), _np(b), "64 heads")
+
+
+def test_degenerate_inputs():
+    """Zero tokens give the bias exactly; zero weights give the bias exactly;
+    without a bias, zero tokens give zeros (the oracle's closed forms)."""
+    heads, S = 2, 300
+    D = heads * 128
+    x = synth.make_tokens(1, S, D, seed=9).to(DEV)
+    w, b = (t.to(DEV) for t in synth.make_qkv_weights(D, seed=9))
+    zx, zw = torch.zeros_like(x), torch.zeros_like(w)
+    for xx, ww, bb, want in ((zx, w, b, b), (x, zw, b, b), (zx, w, None, torch.zeros_like(b))):
+        out = wan_attn.qkv_proj(xx, ww, heads, bias=bb)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(S, 3 * D), want.view(1, 3 * D).expand(S, 3 * D))
+
+
 def test_errors():
     x = torch.zeros((1, 8, 256), dtype=torch.bfloat16, device=DEV)
     w = torch.zeros((768, 256), dtype=torch.bfloat16, device=DEV)
