@@ -19,6 +19,14 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// Tuning defaults (the kernel below reads them, so they come first).
+#ifndef WAN_NORM_MIN_CPT
+#define WAN_NORM_MIN_CPT 2  // two 16-byte chunks of Q and of K per thread: more bytes in flight per CU
+#endif
+#ifndef WAN_NORM_NT
+#define WAN_NORM_NT 3  // non-temporal loads (1) and stores (2): the rows are touched once
+#endif
+
 namespace wan {
 
 namespace {
@@ -161,12 +169,6 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
 hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const float2* tab,
                               int64_t row0, int64_t rows, int S, int T, int H, int W, int D,
                               float eps, float* amax, hipStream_t stream) {
-#ifndef WAN_NORM_MIN_CPT
-#define WAN_NORM_MIN_CPT 2  // two 16-byte chunks of Q and of K per thread: more bytes in flight per CU
-#endif
-#ifndef WAN_NORM_NT
-#define WAN_NORM_NT 3  // non-temporal loads (1) and stores (2): the rows are touched once
-#endif
   const int nchunks = D / 8;
   int cpt = nchunks <= 1024 ? 1 : (nchunks <= 2048 ? 2 : 4);
   cpt = cpt < WAN_NORM_MIN_CPT ? WAN_NORM_MIN_CPT : cpt;
