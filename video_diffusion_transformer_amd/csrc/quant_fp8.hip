@@ -19,6 +19,9 @@ namespace wan {
 
 namespace {
 
+#ifndef WAN_QUANT_NT
+#define WAN_QUANT_NT 3  // non-temporal loads (1) and stores (2) in the quantise pass (+2%)
+#endif
 #ifndef WAN_QUANT_TOK
 #define WAN_QUANT_TOK 128
 #endif
@@ -106,9 +109,26 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
     if (s < S) {
       const uint16_t* row = qkv + ((int64_t)b * S + s) * 3 * (int64_t)D + h * 128 + 8 * ch;
       uint8_t* orow = qk8 + ((int64_t)b * S + s) * 2 * (int64_t)D + h * 128 + 8 * ch;
-      *reinterpret_cast<uint2*>(orow) = quant8(*reinterpret_cast<const u32x4_t*>(row), sq);
-      *reinterpret_cast<uint2*>(orow + D) = quant8(*reinterpret_cast<const u32x4_t*>(row + D), sk);
-      vq = quant8(*reinterpret_cast<const u32x4_t*>(row + 2 * D), sv);
+#if WAN_QUANT_NT & 1
+      const u32x4_t xq = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row));
+      const u32x4_t xk = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + D));
+      const u32x4_t xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 2 * D));
+#else
+      const u32x4_t xq = *reinterpret_cast<const u32x4_t*>(row);
+      const u32x4_t xk = *reinterpret_cast<const u32x4_t*>(row + D);
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(row + 2 * D);
+#endif
+#if WAN_QUANT_NT & 2
+      const uint2 oq = quant8(xq, sq), ok = quant8(xk, sk);
+      __builtin_nontemporal_store(oq.x, reinterpret_cast<uint32_t*>(orow));
+      __builtin_nontemporal_store(oq.y, reinterpret_cast<uint32_t*>(orow) + 1);
+      __builtin_nontemporal_store(ok.x, reinterpret_cast<uint32_t*>(orow + D));
+      __builtin_nontemporal_store(ok.y, reinterpret_cast<uint32_t*>(orow + D) + 1);
+#else
+      *reinterpret_cast<uint2*>(orow) = quant8(xq, sq);
+      *reinterpret_cast<uint2*>(orow + D) = quant8(xk, sk);
+#endif
+      vq = quant8(xv, sv);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -124,8 +144,13 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
   for (int i = 0; i < kParts / 2; ++i) {
     const int c = threadIdx.x + 256 * i;
     const int d = c / kParts, part = c % kParts;
+#if WAN_QUANT_NT & 2
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&vt[d][16 * part]),
+                                reinterpret_cast<u32x4_t*>(vbase + (int64_t)d * S_pad + 16 * part));
+#else
     *reinterpret_cast<u32x4_t*>(vbase + (int64_t)d * S_pad + 16 * part) =
         *reinterpret_cast<const u32x4_t*>(&vt[d][16 * part]);
+#endif
   }
 }
 
