@@ -67,6 +67,7 @@ constexpr int kTile = kBN * kRow;        // 16 KB
 constexpr int kStage = 2 * kTile;        // K tile + V tile
 constexpr int kStages = 2;               // LDS stages (K + V tile each)
 constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag behind the true max
+constexpr float kSumLimit = 256.0f;      // 2^kRescaleSlack: bound on a lane's sum of one tile's probabilities
 constexpr int kWaitVmem0 = 0x0f70;       // s_waitcnt vmcnt(0), other counters unconstrained
 
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
@@ -149,44 +150,6 @@ __device__ __forceinline__ void tile_scores(const TileArgs& a, const unsigned ch
 // tile's max exceeds it by more than the slack. The row sums are rescaled here;
 // returns a bit per query tile whose max moved, with the factor alpha the
 // output accumulator must be scaled by.
-__device__ __forceinline__ unsigned tile_max(const TileArgs& a, int k0, f32x4_t (&acc_s)[4][kQT],
-                                             float (&m_run)[kQT], float (&acc_l)[kQT], float (&alpha)[kQT]) {
-  // Mask keys past the end (only the last tile can have them).
-  if (k0 + kBN > a.S) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (k0 + 16 * t + 4 * a.grp + i >= a.S) {
-#pragma unroll
-          for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
-        }
-  }
-  unsigned moved = 0;
-#pragma unroll
-  for (int u = 0; u < kQT; ++u) {
-    float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
-#pragma unroll
-    for (int t = 1; t < 4; ++t)
-      mx = fmaxf(mx, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
-    // The four lanes of a query column share m_run, so one of them exceeding
-    // m_run + slack with its own 16 scores is the same test as the column max
-    // doing so: the cross-lane reduction is only needed when the max moves.
-    mx *= a.scale_log2;
-    alpha[u] = 1.0f;
-    if (__ballot(mx > m_run[u] + kRescaleSlack)) {
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[u], mx);
-      alpha[u] = __builtin_amdgcn_exp2f(m_run[u] - m_new);
-      m_run[u] = m_new;
-      acc_l[u] *= alpha[u];
-      moved |= 1u << u;
-    }
-  }
-  return moved;
-}
-
 // Scales the output accumulator of the query tiles whose max moved.
 __device__ __forceinline__ void tile_rescale(unsigned moved, const float (&alpha)[kQT], f32x4_t (&acc_o)[8][kQT]) {
 #pragma unroll
@@ -205,10 +168,11 @@ __device__ __forceinline__ void tile_rescale(unsigned moved, const float (&alpha
 // dot product of each packed pair with (1, 1), fp32 sum), so the
 // normalisation matches what PV accumulated; each lane sums its own keys.
 __device__ __forceinline__ void tile_exp(const TileArgs& a, const f32x4_t (&acc_s)[4][kQT], const float (&m_run)[kQT],
-                                         bf16x8_t (&pf)[kQT][2], float (&acc_l)[kQT]) {
+                                         bf16x8_t (&pf)[kQT][2], float (&lt)[kQT]) {
   const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
-  for (int u = 0; u < kQT; ++u)
+  for (int u = 0; u < kQT; ++u) {
+    lt[u] = 0.f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       bf16x8_t v;
@@ -218,11 +182,86 @@ __device__ __forceinline__ void tile_exp(const TileArgs& a, const f32x4_t (&acc_
       pf[u][c] = v;
       // Literal shuffles: extracting the pairs through a bit cast to 32-bit
       // lanes is miscompiled by this clang (every extraction read element 0).
-      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc_l[u], false);
-      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, acc_l[u], false);
-      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, acc_l[u], false);
-      acc_l[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, acc_l[u], false);
+      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, lt[u], false);
+      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, lt[u], false);
+      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, lt[u], false);
+      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, lt[u], false);
     }
+  }
+}
+
+// One query tile redone against a new running max (the rare path of tile_softmax).
+__device__ __forceinline__ void tile_exp_one(const TileArgs& a, const f32x4_t (&acc_s)[4][kQT], float m, int u,
+                                             bf16x8_t (&pf)[kQT][2], float& lt) {
+  const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  lt = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    bf16x8_t v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], a.scale_log2, -m));
+    pf[u][c] = v;
+    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, lt, false);
+    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, lt, false);
+    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, lt, false);
+    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, lt, false);
+  }
+}
+
+// Softmax step with optimistic exponentials: all probabilities of the tile are
+// computed against the running max first. If some lane's sum over its 16 keys
+// of a query tile exceeds 2^slack (or is infinite: on the first tile the
+// running max is the most negative float), a score passed the running max by
+// more than the slack; that query tile is then redone against the new max (the
+// column max of the tile's scores), with the running sum rescaled and the
+// query tile marked for the output rescale. Each probability is at most its
+// lane's sum, so p <= 2^slack on every kept tile: the bound a max test before
+// the exponentials gives, without computing the max where it does not move.
+__device__ __forceinline__ unsigned tile_softmax(const TileArgs& a, int k0, f32x4_t (&acc_s)[4][kQT],
+                                                 float (&m_run)[kQT], float (&acc_l)[kQT], float (&alpha)[kQT],
+                                                 bf16x8_t (&pf)[kQT][2]) {
+  // Mask keys past the end (only the last tile can have them).
+  if (k0 + kBN > a.S) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + 16 * t + 4 * a.grp + i >= a.S) {
+#pragma unroll
+          for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
+        }
+  }
+  float lt[kQT];
+  tile_exp(a, acc_s, m_run, pf, lt);
+  bool over = false;
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) over = over || lt[u] > kSumLimit;
+  unsigned moved = 0;
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) alpha[u] = 1.0f;
+  if (__ballot(over)) {
+#pragma unroll
+    for (int u = 0; u < kQT; ++u)
+      if (__ballot(lt[u] > kSumLimit)) {
+        float mx = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
+#pragma unroll
+        for (int t = 1; t < 4; ++t)
+          mx = fmaxf(mx, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
+        mx *= a.scale_log2;
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[u], mx);
+        alpha[u] = __builtin_amdgcn_exp2f(m_run[u] - m_new);
+        m_run[u] = m_new;
+        acc_l[u] *= alpha[u];
+        moved |= 1u << u;
+        tile_exp_one(a, acc_s, m_new, u, pf, lt[u]);
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) acc_l[u] += lt[u];
+  return moved;
 }
 
 // O^T (channels x queries) += V^T P^T over one tile: 8 channel tiles x 2 key
@@ -325,7 +364,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc_o[i][u] = f32x4_t{};
     acc_l[u] = 0.0f;
-    m_run[u] = -INFINITY;
+    m_run[u] = -3.0e38f;  // finite: s - m_run is +inf (or -inf for masked keys), never NaN
   }
 
   float alpha[kQT];
@@ -348,9 +387,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // 1 copy
     }
-    const unsigned moved = tile_max(a, kt * kBN, acc_s, m_run, acc_l, alpha);
+    const unsigned moved = tile_softmax(a, kt * kBN, acc_s, m_run, acc_l, alpha, pf);
     if (moved) tile_rescale(moved, alpha, acc_o);
-    tile_exp(a, acc_s, m_run, pf, acc_l);
     // Let the next tile's direct-to-LDS writes finish before the transposed V
     // reads: measured, the PV phase runs faster without those writes competing
     // for the LDS, and the loads have had the score and softmax phases to land.
