@@ -150,6 +150,10 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
   };
 
   const int nu = (S + kBN - 1) / kBN;
+  // P of the current unit in e4m3. Each word is written as two halves by two
+  // conversions; the first keeps the other half of the word it is given, so
+  // it is given the word it replaces (kept across units: no zeroing moves).
+  i32x8_t pf[2] = {};
   issue_unit(0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
@@ -168,7 +172,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
       const int r = 32 * (l16 >> 2) + 4 * t + (l16 & 3);
       const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(ks + k_swz(r, 2 * grp));
       const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(ks + k_swz(r, 2 * grp + 1));
-      const i32x8_t a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       acc_s[t][0] = mfma_fp8(a, qf[0], f32x4_t{});
       acc_s[t][1] = mfma_fp8(a, qf[1], f32x4_t{});
     }
@@ -181,7 +185,6 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
           if (k0 + 32 * grp + 4 * t + i >= S) acc_s[t][0][i] = acc_s[t][1][i] = -INFINITY;
     }
 
-    i32x8_t pf[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float mx = fmaxf(acc_s[0][u][0], acc_s[0][u][1]);
@@ -212,7 +215,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(acc_s[t][u][i], c_log2, -m_shift));
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[u][t], false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pf[u][t] = w;
       }
@@ -225,7 +228,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
       const int r = 16 * dt + l16;
       const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(vs + v_swz(r, 2 * grp));
       const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(vs + v_swz(r, 2 * grp + 1));
-      const i32x8_t a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       acc_o[dt][0] = mfma_fp8(a, pf[0], acc_o[dt][0]);
       acc_o[dt][1] = mfma_fp8(a, pf[1], acc_o[dt][1]);
     }
