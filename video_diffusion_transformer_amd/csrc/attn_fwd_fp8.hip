@@ -187,11 +187,17 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      float mx = fmaxf(acc_s[0][u][0], acc_s[0][u][1]);
+      // Two chains of three-input maxima (v_max3_f32): 17 instructions for the
+      // 32 scores; the empty asm keeps the compiler from re-balancing them into
+      // a tree of two-input maxima (23 instructions).
+      float m1 = fmaxf(acc_s[0][u][0], acc_s[0][u][1]), m2 = fmaxf(acc_s[0][u][2], acc_s[0][u][3]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = (t == 0 ? 2 : 0); i < 4; i += 2) mx = fmaxf(mx, fmaxf(acc_s[t][u][i], acc_s[t][u][i + 1]));
+      for (int t = 1; t < 8; ++t) {
+        m1 = fmaxf(m1, fmaxf(acc_s[t][u][0], acc_s[t][u][1]));
+        m2 = fmaxf(m2, fmaxf(acc_s[t][u][2], acc_s[t][u][3]));
+        asm("" : "+v"(m1), "+v"(m2));
+      }
+      float mx = fmaxf(m1, m2);
       // Lanes l, l^16, l^32, l^48 share the query and its m_run: testing each
       // lane's own max is the same as testing the column max, so the
       // cross-lane reduction runs only when the max moves.
