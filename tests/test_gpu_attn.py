@@ -57,6 +57,24 @@ def test_peaky_softmax_rescales():
     _full_compare(qkv.to(torch.bfloat16), 2, "peaky")
 
 
+def test_running_max_moves_late_and_by_steps():
+    """Keys whose scores grow along the sequence (a ramp added to K along Q's
+    mean direction), so the running max passes its slack on many later tiles,
+    and one key in the last tile that dominates every query: the rescale-and-
+    redo path runs on late tiles, including a ragged last tile."""
+    heads, S = 2, 700
+    D = heads * 128
+    qkv = synth.make_qkv(1, S, heads, seed=13).float()
+    q = qkv[0, :, :D].reshape(S, heads, 128)
+    d = q.mean(dim=0)
+    d = d / d.norm(dim=-1, keepdim=True)
+    ramp = torch.linspace(0.0, 200.0, S).view(S, 1, 1)
+    k = qkv[0, :, D:2 * D].reshape(S, heads, 128) + ramp * d
+    k[S - 3] = 400.0 * d
+    qkv[0, :, D:2 * D] = k.reshape(S, D)
+    _full_compare(qkv.to(torch.bfloat16), heads, "late max")
+
+
 def test_closed_forms():
     heads, S = 2, 333
     D = heads * 128
