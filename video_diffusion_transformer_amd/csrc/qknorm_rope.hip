@@ -9,7 +9,10 @@
 // halves. Q and K stay in registers between the reduction and the store: every
 // element is read once and written once (HBM-bound, ~2 FLOP/byte). The full-width
 // mean square is a wavefront butterfly reduction followed by a cross-wave sum in
-// LDS. V is never written.
+// LDS. V is never written. The token's 64 rotary (cos, sin) pairs are gathered
+// from the three per-axis tables once per workgroup, by one wave, into LDS:
+// read per thread and per chunk from the tables instead, they cost 4% of the
+// kernel's bandwidth (eight 8-byte loads per thread against four 16-byte Q/K loads).
 //
 // The fp8 variant (Amax) also takes, in the same pass, max |x| of the rounded Q
 // and K it writes and of V (read once for it), and folds them into amax[0..2]:
@@ -57,6 +60,15 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
   uint16_t* qrow = qkv + row * (3 * (int64_t)D);
   uint16_t* krow = qrow + D;
 
+  // The token's 64 rotary (cos, sin) pairs (22 frame, 21 row, 21 column), gathered once by the
+  // first wave into LDS; published by the barrier of the reduction below.
+  __shared__ __attribute__((aligned(16))) float2 rot[64];
+  if (threadIdx.x < 64) {
+    const int p = threadIdx.x;
+    rot[p] = p < kPairsT ? tab[f * kPairsT + p]
+                         : (p < kPairsT + kPairsH ? tab[offH + y * kPairsH + (p - kPairsT)]
+                                                  : tab[offW + x * kPairsW + (p - kPairsT - kPairsH)]);
+  }
   u32x4_t qv[CPT], kv[CPT];
   float sq = 0.f, sk = 0.f, mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll
@@ -99,9 +111,17 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
   const float rq = rsqrtf(sq * inv_d + eps);
   const float rk = rsqrtf(sk * inv_d + eps);
 
-  const float2* tt = tab + f * kPairsT;
-  const float2* th = tab + offH + y * kPairsH;
-  const float2* tw = tab + offW + x * kPairsW;
+  // Chunk c holds pairs 4 (c % 16) .. +3 of its head; c = threadIdx.x + i * blockDim.x with
+  // blockDim a multiple of 64, so all chunks of this thread use the same four pairs.
+  float2 cs4[4];
+  {
+    const float4* r = reinterpret_cast<const float4*>(rot) + 2 * (threadIdx.x & 15);
+    const float4 a0 = r[0], a1 = r[1];
+    cs4[0] = make_float2(a0.x, a0.y);
+    cs4[1] = make_float2(a0.z, a0.w);
+    cs4[2] = make_float2(a1.x, a1.y);
+    cs4[3] = make_float2(a1.z, a1.w);
+  }
 
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -109,12 +129,10 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
     if (c < nchunks) {
       const u32x4_t g1 = *reinterpret_cast<const u32x4_t*>(gq + 8 * c);
       const u32x4_t g2 = *reinterpret_cast<const u32x4_t*>(gk + 8 * c);
-      const int p0 = (4 * c) & 63;  // first rotary pair of this chunk within its head
       u32x4_t qo, ko;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int p = p0 + j;
-        const float2 cs = p < kPairsT ? tt[p] : (p < kPairsT + kPairsH ? th[p - kPairsT] : tw[p - kPairsT - kPairsH]);
+        const float2 cs = cs4[j];
         // norm, x gamma, bf16 rounding point
         const uint32_t nq = pack_bf16x2(bf16_lo(qv[i][j]) * rq * bf16_lo(g1[j]),
                                         bf16_hi(qv[i][j]) * rq * bf16_hi(g1[j]));
