@@ -122,7 +122,7 @@ def test_fp8_720p_sampled_rows():
             assert np.abs(got_lse[b, h] - l_ref).max() <= 5e-2
 
 
-def _fused_vs_two_calls(B, grid, heads, seed, device_gen=False):
+def _fused_vs_two_calls(B, grid, heads, seed, device_gen=False, **norm_args):
     """wan_qknorm_rope_quant_fp8 against wan_qknorm_rope then wan_qkv_quant_fp8
     on copies of the same buffer: every output bit-identical."""
     T, H, W = grid
@@ -130,10 +130,10 @@ def _fused_vs_two_calls(B, grid, heads, seed, device_gen=False):
     qkv = synth.make_qkv(B, S, heads, seed=seed, device=DEV if device_gen else "cpu").to(DEV)
     gq, gk = synth.make_gammas(heads * 128, seed=seed, device=DEV)
     a = qkv.clone()
-    wan_attn.qknorm_rope(a, gq, gk, grid, heads)
+    wan_attn.qknorm_rope(a, gq, gk, grid, heads, **norm_args)
     fa = wan_attn.qkv_quant_fp8(a, heads)
     b = qkv
-    fb = wan_attn.qknorm_rope_quant_fp8(b, gq, gk, grid, heads)
+    fb = wan_attn.qknorm_rope_quant_fp8(b, gq, gk, grid, heads, **norm_args)
     torch.cuda.synchronize()
     assert torch.equal(a, b), "in-place bf16 Q/K differ"
     for name in ("amax", "scales", "qk8"):
@@ -146,6 +146,12 @@ def _fused_vs_two_calls(B, grid, heads, seed, device_gen=False):
                                           (2, (3, 7, 11), 40), (1, (5, 9, 13), 8)])
 def test_fused_norm_quant_equals_two_calls(B, grid, heads):
     _fused_vs_two_calls(B, grid, heads, seed=sum(grid) + heads)
+
+
+def test_fused_norm_quant_passes_eps_and_theta():
+    """Non-default eps and theta reach the fused norm pass the same way as the
+    plain norm call (whose parity with these values the norm tests check)."""
+    _fused_vs_two_calls(2, (3, 4, 5), 2, seed=31, eps=1e-2, theta=500.0)
 
 
 def test_fused_norm_quant_matches_oracle():

@@ -24,7 +24,7 @@ def _np(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def _check(gpu_qkv, ref, heads, grid, rows, D, workload_gates=True):
+def _check(gpu_qkv, ref, heads, grid, rows, D, workload_gates=True, theta=1e4):
     T, H, W = grid
     S = T * H * W
     tok = rows % S
@@ -32,7 +32,7 @@ def _check(gpu_qkv, ref, heads, grid, rows, D, workload_gates=True):
     flat = gpu_qkv.reshape(-1, 3 * D)
     for name, off in (("q", 0), ("k", D)):
         g = flat[rows, off:off + D]
-        ok, exact, err = norm_rope_candidates_match(g, ref, name, heads, 128, f, y, x)
+        ok, exact, err = norm_rope_candidates_match(g, ref, name, heads, 128, f, y, x, theta=theta)
         bad = np.argwhere(~ok)
         assert ok.all(), f"{name}: {len(bad)} elements outside the candidate set, first {bad[:5].tolist()}"
         assert exact >= 0.9999, f"{name}: only {exact} equal to the nearest oracle value"
@@ -71,6 +71,25 @@ def test_tiny_config():
                                           (2, (2, 3, 5), 40), (1, (2, 2, 2), 256)])
 def test_ragged_and_odd_shapes(B, grid, heads):
     _run_full(B, grid, heads, seed=sum(grid) + heads)
+
+
+def test_non_default_eps_and_theta():
+    """eps and theta reach the kernel: with eps = 1e-2 and theta = 500 the
+    oracle's output differs from the default-parameter one in most elements,
+    and the kernel must match the former."""
+    B, grid, heads = 2, (3, 4, 5), 2
+    eps, theta = 1e-2, 500.0
+    S, D = 3 * 4 * 5, heads * 128
+    qkv = synth.make_qkv(B, S, heads, seed=31)
+    gq, gk = synth.make_gammas(D, seed=31)
+    host = _np(qkv)
+    ref = wan_ref.qknorm_rope_ref(host, _np(gq), _np(gk), grid, heads, 128, eps=eps, theta=theta)
+    dflt = wan_ref.qknorm_rope_ref(host, _np(gq), _np(gk), grid, heads, 128)
+    assert np.mean(ref["out16_q"] != dflt["out16_q"]) > 0.5
+    d = qkv.to(DEV)
+    wan_attn.qknorm_rope(d, gq.to(DEV), gk.to(DEV), grid, heads, eps=eps, theta=theta)
+    torch.cuda.synchronize()
+    _check(_np(d), ref, heads, grid, np.arange(B * S), D, theta=theta)
 
 
 def test_heterogeneous_head_magnitudes_and_gammas():
