@@ -49,6 +49,21 @@ def test_ragged_shapes(B, S, heads):
     _full_compare(synth.make_qkv(B, S, heads, seed=S + heads), heads, f"B{B} S{S} h{heads}")
 
 
+@pytest.mark.parametrize("scale", [0.03, 0.25])
+def test_non_default_softmax_scale(scale):
+    """The softmax scale reaches the kernel: against the oracle at that scale
+    (whose output is far from the default-scale one: max difference > 0.5)."""
+    heads, S = 2, 200
+    qkv = synth.make_qkv(1, S, heads, seed=17)
+    out, lse = wan_attn.attn_fwd(qkv.to(DEV), heads, lse=True, softmax_scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = wan_ref.attn_packed_ref(_np(qkv), heads, 128, scale)
+    o_def, _ = wan_ref.attn_packed_ref(_np(qkv), heads, 128, SCALE)
+    assert attn_error_stats(o_def, o_ref)["max"] > 0.5
+    assert_gates(attn_error_stats(_np(out), o_ref), BF16_GATES, f"scale {scale}")
+    assert np.abs(_np(lse) - l_ref).max() <= LSE_ABS
+
+
 def test_peaky_softmax_rescales():
     """Q x 8 makes the softmax nearly one-hot and forces the running max to
     move between tiles."""

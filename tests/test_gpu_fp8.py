@@ -57,12 +57,12 @@ def test_quant_all_zero_and_outlier():
     assert list(f.scales.cpu().numpy()) == [1.0, float(np.float32(448.0) / np.float32(1000.0)), 1.0]
 
 
-def _check_attn(qkv, heads, what, rows=None):
+def _check_attn(qkv, heads, what, rows=None, scale=SCALE):
     f, r = _check_quant(qkv, heads) if rows is None else (wan_attn.qkv_quant_fp8(qkv.to(DEV), heads), None)
-    out, lse = wan_attn.attn_fwd_fp8(f, lse=True)
+    out, lse = wan_attn.attn_fwd_fp8(f, lse=True, softmax_scale=scale)
     torch.cuda.synchronize()
     deq = r["deq"]
-    o_ref, l_ref = wan_ref.attn_packed_ref(deq, heads, 128, SCALE)
+    o_ref, l_ref = wan_ref.attn_packed_ref(deq, heads, 128, scale)
     st = attn_error_stats(_np(out), o_ref)
     assert_gates(st, FP8_GATES, what)
     assert np.abs(_np(lse) - l_ref).max() <= 5e-2, what
@@ -77,6 +77,12 @@ def test_tiny_fp8_attention():
 @pytest.mark.parametrize("B,S,heads", [(1, 1, 1), (1, 129, 2), (2, 333, 3), (1, 1000, 2), (2, 256, 40)])
 def test_ragged_fp8_attention(B, S, heads):
     _check_attn(synth.make_qkv(B, S, heads, seed=3 * S + heads), heads, f"fp8 B{B} S{S} h{heads}")
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.25])
+def test_fp8_non_default_softmax_scale(scale):
+    """The softmax scale reaches the fp8 kernel (the oracle runs at the same scale)."""
+    _check_attn(synth.make_qkv(1, 200, 2, seed=17), 2, f"fp8 scale {scale}", scale=scale)
 
 
 def test_peaky_fp8_attention():
