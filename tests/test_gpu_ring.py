@@ -133,6 +133,28 @@ def test_chunk_merge_equals_chunk_then_merge(B, S, heads, bounds):
     assert np.abs(_np(b_lse) - l_ref).max() <= LSE_ABS
 
 
+def test_ring_non_default_softmax_scale():
+    """The softmax scale reaches both chunk kernels: chunks at scale 0.03
+    merged (separately and in the epilogue) equal full attention at 0.03."""
+    B, S, heads, scale = 1, 500, 2, 0.03
+    D = heads * 128
+    qkv = synth.make_qkv(B, S, heads, seed=23).to(DEV)
+    acc = torch.zeros((B, S, D), dtype=torch.float32, device=DEV)
+    lse = torch.full((B, heads, S), -math.inf, dtype=torch.float32, device=DEV)
+    f_acc, f_lse = acc.clone(), lse.clone()
+    a16, f16 = (torch.empty((B, S, D), dtype=torch.bfloat16, device=DEV) for _ in range(2))
+    for lo, hi in ((0, 130), (130, 333), (333, 500)):
+        kv = qkv[:, lo:hi].contiguous()
+        o, l = wan_attn.attn_fwd_chunk(qkv, kv, heads, softmax_scale=scale)
+        wan_attn.attn_merge(acc, lse, o, l, heads, out_bf16=a16)
+        wan_attn.attn_fwd_chunk_merge(qkv, kv, f_acc, f_lse, heads, softmax_scale=scale, out_bf16=f16)
+    torch.cuda.synchronize()
+    o_ref, l_ref = wan_ref.attn_packed_ref(_np(qkv), heads, 128, scale)
+    for out, l, what in ((a16, lse, "chunk + merge"), (f16, f_lse, "chunk with merge")):
+        assert_gates(attn_error_stats(_np(out), o_ref), BF16_GATES, what)
+        assert np.abs(_np(l) - l_ref).max() <= LSE_ABS, what
+
+
 def test_chunk_merge_errors():
     buf = torch.zeros(2 * 8 * 768, dtype=torch.bfloat16, device=DEV)
     q = buf[:8 * 768].view(1, 8, 768)
