@@ -68,6 +68,7 @@ constexpr int kStage = 2 * kTile;        // K tile + V tile
 constexpr int kStages = 2;               // LDS stages (K + V tile each)
 constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag behind the true max
 constexpr float kSumLimit = 256.0f;      // 2^kRescaleSlack: bound on a lane's sum of one tile's probabilities
+static_assert(kSumLimit == static_cast<float>(1 << static_cast<int>(kRescaleSlack)), "the sum limit is 2^slack");
 constexpr int kWaitVmem0 = 0x0f70;       // s_waitcnt vmcnt(0), other counters unconstrained
 
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
