@@ -49,6 +49,12 @@ def test_ragged_shapes(B, S, heads):
     _full_compare(synth.make_qkv(B, S, heads, seed=S + heads), heads, f"B{B} S{S} h{heads}")
 
 
+def test_largest_head_count():
+    """256 heads (the largest the library accepts): the largest row stride and
+    head offset the kernel addresses."""
+    _full_compare(synth.make_qkv(1, 70, 256, seed=256), 256, "256 heads")
+
+
 @pytest.mark.parametrize("scale", [0.03, 0.25])
 def test_non_default_softmax_scale(scale):
     """The softmax scale reaches the kernel: against the oracle at that scale

@@ -79,6 +79,11 @@ def test_ragged_fp8_attention(B, S, heads):
     _check_attn(synth.make_qkv(B, S, heads, seed=3 * S + heads), heads, f"fp8 B{B} S{S} h{heads}")
 
 
+def test_fp8_largest_head_count():
+    """256 heads (the largest the library accepts) through quantisation and fp8 attention."""
+    _check_attn(synth.make_qkv(1, 130, 256, seed=257), 256, "fp8 256 heads")
+
+
 @pytest.mark.parametrize("scale", [0.03, 0.25])
 def test_fp8_non_default_softmax_scale(scale):
     """The softmax scale reaches the fp8 kernel (the oracle runs at the same scale)."""
