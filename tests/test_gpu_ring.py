@@ -41,7 +41,8 @@ def _ring(q_src, kv_full, heads, bounds, order=None):
 
 
 @pytest.mark.parametrize("B,S,heads,bounds", [(1, 500, 2, [0, 130, 333, 500]), (2, 777, 3, [0, 1, 400, 777]),
-                                              (1, 300, 40, [0, 150, 300]), (1, 1000, 2, [0, 64, 128, 640, 1000])])
+                                              (1, 300, 40, [0, 150, 300]), (1, 1000, 2, [0, 64, 128, 640, 1000]),
+                                              (1, 70, 256, [0, 30, 70])])
 def test_ring_merge_equals_full_attention(B, S, heads, bounds):
     qkv = synth.make_qkv(B, S, heads, seed=S + heads).to(DEV)
     acc, acc_lse, out16 = _ring(qkv, qkv, heads, bounds)
