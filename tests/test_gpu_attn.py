@@ -133,6 +133,31 @@ def test_deterministic_and_layout_independent():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
+def test_side_stream_ordering():
+    """Norm + RoPE and attention issued on a side stream, right after torch work
+    on that stream fills the buffer and with no synchronisation in between,
+    give the same bits as the default-stream path: the library launches on the
+    stream it is handed."""
+    B, S, heads, grid = 1, 300, 2, (3, 10, 10)
+    D = heads * 128
+    host = synth.make_qkv(B, S, heads, seed=77)
+    gq, gk = synth.make_gammas(D, seed=77, device=DEV)
+    ref_buf = host.to(DEV)
+    wan_attn.qknorm_rope(ref_buf, gq, gk, grid, heads)
+    ref = wan_attn.attn_fwd(ref_buf, heads)
+    torch.cuda.synchronize()
+    src = host.to(DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        buf = torch.empty_like(src)
+        buf.copy_(src * 1.0)               # queued on the side stream
+        wan_attn.qknorm_rope(buf, gq, gk, grid, heads)
+        out = wan_attn.attn_fwd(buf, heads)
+    side.synchronize()
+    assert torch.equal(buf, ref_buf) and torch.equal(out, ref)
+
+
 def test_errors_and_empty():
     qkv = torch.zeros((1, 16, 768), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(wan_attn.WanError) as e:
