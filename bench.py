@@ -6,19 +6,27 @@ A step is the whole hot path over one batch of synthetic input already resident
 in HBM: in-place Q/K RMSNorm + bf16 rounding + 3-D RoPE on the packed [Q|K|V]
 buffer, then bidirectional attention over every token (the fp8 workload adds
 the per-tensor e4m3 quantisation, its amax taken in the norm pass, and runs
-attention on fp8 MFMA). W untimed
-warm-up steps, then K timed steps between device synchronisations. One JSON
-line is printed.
+attention on fp8 MFMA). Before every step Q and K are restored from a pristine
+device copy (the norm works in place, so each step sees the same input, normalised
+once); the restore is outside the timed events. W untimed warm-up steps, then K
+timed steps. One JSON line is printed.
 
   value       attention FLOP of one step (4 * B * heads * S^2 * 128) divided by
-              the measured time of the whole step, in TFLOP/s.
+              the measured time of the whole step (HIP events on the stream the
+              kernels run on, from the first kernel of the step to the end of
+              attention), in TFLOP/s.
   roofline    the dominant kernel (attention): algorithmic FLOP per launch over
-              its average launch time from HIP events recorded on the stream it
-              runs on, against the dense MFMA peak of its dtype; ``traffic`` is
-              the HBM bytes per launch from the committed rocprofv3 counter
-              summary when it was taken on the current kernel source, else null.
-  cpu_baseline the fp64 numpy oracle on the host cores, on a bounded sample of
-              the same workload (query rows of one head against all keys).
+              its average launch time from HIP events recorded on its stream,
+              against the dense MFMA peak of its dtype; ``traffic`` is the HBM
+              bytes per launch from the committed rocprofv3 counter summary when
+              it was taken on the current kernel source, else null.
+  720p, 720p_fp8, long
+              (with the default --workload 480p) the same step on the other
+              workloads, a few steps each: step time, attention and norm (or
+              fused fp8 prep) against their rooflines.
+  cpu_baseline the fp64 numpy oracle on the host cores: attention on a bounded
+              sample (query rows of one head against all keys) and the norm +
+              RoPE over the full 480p tensor.
   ring_share  (bf16 workloads) one GPU's share of ring attention with the
               sequence split over --ring-cp ranks: S/cp queries against cp
               K/V chunks, each round folded into the accumulator by the
@@ -44,6 +52,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "attn_fwd_fp8": "attn_fwd_fp8.hip",
                   "qknorm_rope": "qknorm_rope.hip", "qkv_proj": "qkv_proj.hip"}
+EXTRA_WORKLOADS = ("720p", "720p_fp8", "long")
 
 
 def kernel_source_hash(name):
@@ -64,17 +73,31 @@ def committed_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s=12.0):
-    """Time the oracle's attention on query rows of (b=0, h=0) against all S
-    keys until about ``budget_s`` seconds of CPU work are done."""
+    """The oracle on the host cores: its attention on query rows of (b=0,
+    h=0) against all S keys until about ``budget_s`` seconds of CPU work are
+    done, and its norm + RoPE over the full 480p tensor (chunks of 4096
+    tokens, one chunk per host thread at a time)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
 
     from oracle import wan_ref
     from video_diffusion_transformer_amd import synth
+    from video_diffusion_transformer_amd.configs import WORKLOADS
 
     cores = len(os.sched_getaffinity(0))
-    torch.manual_seed(0)
     gen = torch.Generator().manual_seed(w.seed)
     k = torch.randn((w.S, 128), generator=gen).to(torch.bfloat16).double().numpy()
     v = torch.randn((w.S, 128), generator=gen).to(torch.bfloat16).double().numpy()
@@ -85,11 +108,34 @@ def cpu_baseline(w, budget_s=12.0):
         rows += batch
     dt = time.perf_counter() - t0
     flop = 4.0 * rows * w.S * 128
-    del synth
+    del k, v
+
+    n = WORKLOADS["480p"]
+    qkv = synth.make_qkv(n.B, n.S, n.heads, seed=n.seed).view(n.B * n.S, 3 * n.D)
+    gq, gk = (g.double().numpy() for g in synth.make_gammas(n.D, seed=n.seed))
+    chunk = 4096
+
+    def norm_chunk(r0):
+        r1 = min(r0 + chunk, n.B * n.S)
+        x = qkv[r0:r1, :2 * n.D].double().numpy()
+        wan_ref.qknorm_rope_tokens_ref(x, np.arange(r0, r1) % n.S, gq, gk, (n.T, n.H, n.W), n.heads, 128)
+        return r1 - r0
+
+    t1 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        tokens = sum(ex.map(norm_chunk, range(0, n.B * n.S, chunk)))
+    dn = time.perf_counter() - t1
+    del qkv
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} query rows of head 0 x all {w.S} keys, fp64 numpy (BLAS threads = "
-                      f"{cores}), {dt:.1f} s; full-step time extrapolated: "
-                      f"{w.attn_flop() / (flop / dt):.0f} s"}
+            "cpu_model": cpu_model(),
+            "sample": f"attention: {rows} query rows of head 0 x all {w.S} keys, fp64 numpy (BLAS threads = "
+                      f"{cores}), {dt:.1f} s; full-step attention time extrapolated: "
+                      f"{w.attn_flop() / (flop / dt):.0f} s",
+            "qknorm_rope_480p": {"seconds": round(dn, 2), "tokens": tokens, "threads": cores,
+                                 "GB/s": round(n.norm_bytes() / dn / 1e9, 3),
+                                 "note": "exact time of the oracle's norm + RoPE over the whole 480p tensor "
+                                         "(B=2, S=32760, 40 heads), chunks of 4096 tokens on a pool of host "
+                                         "threads"}}
 
 
 def ring_share(w, qkv, cp, reps=3):
@@ -180,51 +226,27 @@ def qkv_proj(w, dev, reps=3):
             "traffic": committed_traffic("qkv_proj", w.name)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="480p", choices=["480p", "720p", "720p_fp8", "long", "tiny"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fp8-unfused", action="store_true",
-                    help="fp8 workload: run norm + RoPE and the quantisation as two calls (separate amax pass) "
-                         "instead of wan_qknorm_rope_quant_fp8")
-    ap.add_argument("--ring-cp", type=int, default=8, metavar="CP",
-                    help="also time one GPU's share of ring attention with the sequence split over CP ranks "
-                         "(bf16 workloads; 0 to skip)")
-    ap.add_argument("--proj-reps", type=int, default=3, metavar="N",
-                    help="timed calls of the QKV projection on the workload's tokens (bf16 workloads; 0 to skip)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="before the steps, run one plain device copy of MIB MiB (its hardware "
-                         "counters scale FETCH_SIZE / WRITE_SIZE to bytes)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
-              "path is a design note only).", file=sys.stderr)
-        sys.exit(2)
-
+def run_steps(w, dev, steps, warmup, fp8_unfused=False):
+    """Allocate the workload's buffers and run warm-up + timed steps. Returns
+    (timings, qkv) with per-step means in ms of the step and of its phases."""
     import torch
 
     from video_diffusion_transformer_amd import synth, wan_attn
-    from video_diffusion_transformer_amd.configs import WORKLOADS
 
-    w = WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     grid = (w.T, w.H, w.W)
     qkv = synth.make_qkv(w.B, w.S, w.heads, seed=w.seed, device=dev)
+    pristine_qk = qkv[..., :2 * w.D].clone()  # V is never written
     gq, gk = synth.make_gammas(w.D, seed=w.seed, device=dev)
     out = torch.empty((w.B, w.S, w.D), dtype=torch.bfloat16, device=dev)
     fp8 = w.dtype == "fp8"
-    if fp8:
-        f8 = wan_attn.fp8_buffers(w.B, w.S, w.heads, dev)
+    f8 = wan_attn.fp8_buffers(w.B, w.S, w.heads, dev) if fp8 else None
     stream = torch.cuda.current_stream(dev)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(ev=None):
+        qkv[..., :2 * w.D].copy_(pristine_qk)  # same input every step; before the step's first event
         if ev: ev[0].record(stream)
-        if fp8 and not args.fp8_unfused:
+        if fp8 and not fp8_unfused:
             wan_attn.qknorm_rope_quant_fp8(qkv, gq, gk, grid, w.heads, out=f8)  # norm + RoPE + amax, quantise
             if ev: ev[1].record(stream)
             if ev: ev[2].record(stream)
@@ -240,6 +262,85 @@ def main():
             wan_attn.attn_fwd(qkv, w.heads, out=out)
         if ev: ev[3].record(stream)
 
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[E() for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t = {"step": sum(e[0].elapsed_time(e[3]) for e in evs) / steps,
+         "norm": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
+         "quant": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
+         "attn": sum(e[2].elapsed_time(e[3]) for e in evs) / steps}
+    del pristine_qk, out, f8
+    return t, qkv
+
+
+def kernel_objects(w, t, fp8_unfused=False):
+    """Roofline objects of the step's kernels from the measured times."""
+    fp8 = w.dtype == "fp8"
+    dtype = "fp8" if fp8 else "bf16"
+    flop = w.attn_flop()
+    attn_tflops = flop / (t["attn"] * 1e-3) / 1e12
+    kname = "attn_fwd_fp8" if fp8 else "attn_fwd"
+    objs = {"attention": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS[dtype],
+                          "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS[dtype], 4),
+                          "traffic": committed_traffic(kname, w.name), "kernel": kname,
+                          "ms_per_launch": round(t["attn"], 4), "flop_per_launch": flop}}
+    if fp8 and not fp8_unfused:
+        # one call: norm + RoPE + amax (reads Q, K, V; writes Q, K), then the
+        # quantisation (reads Q, K, V; writes e4m3 Q, K, V^T)
+        prep_bytes = w.B * w.S * w.D * (8 + 2 + 6 + 3)
+        gbs = prep_bytes / (t["norm"] * 1e-3) / 1e9
+        objs["qknorm_rope_quant_fp8"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                         "ms_per_launch": round(t["norm"], 4), "bytes_per_launch": prep_bytes}
+    else:
+        gbs = w.norm_bytes() / (t["norm"] * 1e-3) / 1e9
+        objs["qknorm_rope"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(gbs / PEAK_HBM_GBS, 4), "ms_per_launch": round(t["norm"], 4),
+                               "bytes_per_launch": w.norm_bytes(),
+                               "traffic": committed_traffic("qknorm_rope", w.name)}
+        if fp8:
+            objs["quant_ms_per_launch"] = round(t["quant"], 4)
+    return objs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="480p", choices=["480p", "720p", "720p_fp8", "long", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-unfused", action="store_true",
+                    help="fp8 workload: run norm + RoPE and the quantisation as two calls (separate amax pass) "
+                         "instead of wan_qknorm_rope_quant_fp8")
+    ap.add_argument("--ring-cp", type=int, default=8, metavar="CP",
+                    help="also time one GPU's share of ring attention with the sequence split over CP ranks "
+                         "(bf16 workloads; 0 to skip)")
+    ap.add_argument("--proj-reps", type=int, default=3, metavar="N",
+                    help="timed calls of the QKV projection on the workload's tokens (bf16 workloads; 0 to skip)")
+    ap.add_argument("--config-steps", type=int, default=5, metavar="N",
+                    help="timed steps of each other workload (720p, 720p_fp8, long) reported next to the 480p "
+                         "headline; 0 to skip them")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, run one plain device copy of MIB MiB (its hardware "
+                         "counters scale FETCH_SIZE / WRITE_SIZE to bytes)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
+              "path is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from video_diffusion_transformer_amd.configs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
     if args.copy_calibration:
         n = args.copy_calibration * 1024 * 1024
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -247,71 +348,50 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[E() for _ in range(4)] for _ in range(args.steps)]
-    t0 = E()
-    t1 = E()
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    quant_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
+    t, qkv = run_steps(w, dev, args.steps, args.warmup, args.fp8_unfused)
+    fp8 = w.dtype == "fp8"
     dtype = "fp8" if fp8 else "bf16"
     flop = w.attn_flop()
-    attn_tflops = flop / (attn_ms * 1e-3) / 1e12
-    norm_gbs = w.norm_bytes() / (norm_ms * 1e-3) / 1e9
-    kname = "attn_fwd_fp8" if fp8 else "attn_fwd"
-    traffic = committed_traffic(kname, w.name)
+    objs = kernel_objects(w, t, args.fp8_unfused)
     rec = {
         "metric": "attention TFLOP/s per DiT self-attention step (QK-norm+RoPE then bidirectional attention)",
-        "value": round(flop / (ms * 1e-3) / 1e12, 2),
+        "value": round(flop / (t["step"] * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(t["step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": f"wan2.2-a14b-{w.name}", "B": w.B, "grid_THW": list(grid), "S": w.S,
+        "config": {"workload": f"wan2.2-a14b-{w.name}", "B": w.B, "grid_THW": [w.T, w.H, w.W], "S": w.S,
                    "heads": w.heads, "head_dim": w.head_dim},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS[dtype],
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS[dtype], 4),
-                     "traffic": traffic, "kernel": kname, "ms_per_launch": round(attn_ms, 4),
-                     "flop_per_launch": flop},
-        "qknorm_rope": {"bound": "hbm", "achieved": round(norm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(norm_gbs / PEAK_HBM_GBS, 4), "ms_per_launch": round(norm_ms, 4),
-                        "bytes_per_launch": w.norm_bytes(),
-                        "traffic": committed_traffic("qknorm_rope", w.name)},
+        "roofline": objs.pop("attention"),
     }
-    if fp8 and not args.fp8_unfused:
-        # one call: norm + RoPE + amax (reads Q, K, V; writes Q, K), then the
-        # quantisation (reads Q, K, V; writes e4m3 Q, K, V^T)
-        del rec["qknorm_rope"]
-        prep_bytes = w.B * w.S * w.D * (8 + 2 + 6 + 3)
-        rec["qknorm_rope_quant_fp8"] = {
-            "bound": "hbm", "achieved": round(prep_bytes / (norm_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(prep_bytes / (norm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "ms_per_launch": round(norm_ms, 4), "bytes_per_launch": prep_bytes}
-    elif fp8:
-        rec["quant_ms_per_launch"] = round(quant_ms, 4)
+    rec.update(objs)
     if args.ring_cp:
         ring = ring_share(w, qkv, args.ring_cp)
         if ring:
             rec["ring_share"] = ring
+    del qkv
+    torch.cuda.empty_cache()
     proj = qkv_proj(w, dev, args.proj_reps)
     if proj:
         rec["qkv_proj"] = proj
+    if args.workload == "480p" and args.config_steps > 0:
+        for name in EXTRA_WORKLOADS:
+            x = WORKLOADS[name]
+            tx, q = run_steps(x, dev, args.config_steps, 2)
+            del q
+            torch.cuda.empty_cache()
+            sub = {"workload": f"wan2.2-a14b-{x.name}", "dtype": x.dtype, "B": x.B, "grid_THW": [x.T, x.H, x.W],
+                   "S": x.S, "steps": args.config_steps, "warmup": 2, "ms_per_step": round(tx["step"], 4),
+                   "step_tflops": round(x.attn_flop() / (tx["step"] * 1e-3) / 1e12, 2)}
+            sub.update(kernel_objects(x, tx))
+            rec[name] = sub
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

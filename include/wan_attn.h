@@ -86,6 +86,25 @@ int wan_abi_version(void);
 const char *wan_status_str(int status);
 
 /*
+ * wan_token_grid -- the DiT token grid of a clip ("Optimizing High-Quality
+ * Offline Video Generation", Grounding in an output spec): the pipeline rounds
+ * the frame's height and width down to a multiple of 16; the VAE compresses
+ * space 8x and time 4x (latent frames = (num_frames - 1) / 4 + 1); the DiT
+ * patchifies 2 x 2 in space. So
+ *   T = (num_frames - 1) / 4 + 1,  H = (height / 16 * 16) / 16,  W = (width / 16 * 16) / 16,
+ * and S = T * H * W tokens (832 x 480 at 81 frames: 21 x 30 x 52 = 32,760).
+ *
+ *   width, height  frame size in pixels, >= 0.
+ *   num_frames     >= 1 and num_frames - 1 divisible by 4 (the 4x temporal
+ *                  compression keeps the first frame).
+ *   T, H, W        host int64_t outputs, written only on success.
+ * Pure host arithmetic: no HIP call, no device memory.
+ * Errors: WAN_E_NULL (an output pointer), WAN_E_SHAPE (negative size, or
+ * num_frames not of the form 4k+1), WAN_E_OVERFLOW (T*H*W beyond int64).
+ */
+int wan_token_grid(int64_t width, int64_t height, int64_t num_frames, int64_t *T, int64_t *H, int64_t *W);
+
+/*
  * wan_qkv_proj -- the QKV projection that fills the packed buffer: for every
  * token, [Q | K | V] = x W^T + bias. "Optimize Wan2.2 Dataflow", change 1: the
  * fused QKV projection produces Q, K and V in one shared allocation (the
@@ -155,8 +174,11 @@ int wan_qknorm_rope(void *qkv, const void *gamma_q, const void *gamma_k,
  *   out[b, s, h*128 + i] = sum_t p(s,t) V[b,t,h,i],
  *   p(s,t) = softmax_t( Q[b,s,h,:] . K[b,t,h,:] * softmax_scale )
  * over every key t < S; no mask, no dropout. QK^T and PV run on bf16 MFMA with
- * fp32 accumulation; the softmax is fp32; P is rounded to bf16 for PV and the
- * row sum that normalises the output is the fp32 sum of those bf16 weights.
+ * fp32 accumulation; the softmax is fp32; P is rounded to bf16 for PV. With
+ * lse == NULL the row sum that normalises the output is the fp32 sum of those
+ * bf16 weights; with an lse buffer it is the fp32 sum of the unrounded
+ * probabilities, so that the returned log-sum-exp is that of the scores up to
+ * fp32 rounding (the two differ in the output by at most 2^-9 relative).
  *
  *   qkv            bf16 [B, S, 3*D] packed buffer (normally after
  *                  wan_qknorm_rope); read only.
@@ -294,6 +316,7 @@ int64_t wan_fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim);
  *   s     = (q8 . k8) / (scale_q * scale_k) * softmax_scale      (fp32)
  *   p8    = e4m3(2^8 * exp(s - m)), m a running maximum (fp32 softmax, online)
  *   out   = sum_t p8 v8 / (scale_v * sum_t p8)
+ *   lse   = m + ln(sum_t exp(s - m)), summed in fp32 before the e4m3 rounding
  *
  *   qk8, vt8, scales  as written by wan_qkv_quant_fp8 for the same sizes.
  *   out               bf16 [B, S, D]; must not overlap the inputs.

@@ -1,5 +1,6 @@
 // Host-only test of the C-ABI argument validation (no HIP calls): every error
 // path returns its status before any memory is touched.
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -143,6 +144,30 @@ int main() {
   EXPECT_EQ(validate_qknorm_rope_fp8(nullptr, nullptr, nullptr, 1, 0, 8, 8, 2, 128, 1e-6f, 1e4f, nullptr, nullptr,
                                      nullptr, nullptr, &z),
             WAN_OK);
+  // size products that overflow int64 are reported, never computed: an empty
+  // call with a huge batch, a huge batch times a huge chunk, a huge batch
+  // times the widest head count
+  EXPECT_EQ(validate_attn(nullptr, nullptr, nullptr, INT64_MAX, 0, 256, 128, 0.088f, 2, &z), WAN_OK);
+  EXPECT_EQ(validate_attn(qkv, outb, lseb, INT64_MAX / 256, 1, 256, 128, 0.088f, 2, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, lsea, 1LL << 40, 1, INT32_MAX, 1, 128, 0.088f, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_attn_chunk_fold(qkv, qkv, of32, lsea, outb, 1LL << 40, 1, INT32_MAX, 1, 128, 0.088f, &z),
+            WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, lsea, INT64_MAX / 384, 1, 2, 1, 128, 0.088f, &z), WAN_E_OVERFLOW);
+  EXPECT_EQ(validate_attn_fp8(qk8, vt8, sc, outb, nullptr, INT64_MAX / 256, 1, 256, 128, 0.088f, &z), WAN_E_OVERFLOW);
+  int64_t big = 0;
+  EXPECT_EQ(fp8_vt_bytes(1, INT64_MAX, 1, &big), 0);
+  EXPECT_EQ(fp8_vt_bytes(INT64_MAX / 128, 256, 1, &big), 0);
+  // NaN scalars are rejected (the check reads the bit pattern, so it also
+  // holds in code compiled with finite-math assumptions)
+  volatile float nan = NAN;
+  EXPECT_EQ(validate_attn(qkv, outb, nullptr, 1, 16, 2, 128, nan, 2, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn(nullptr, nullptr, nullptr, 0, 16, 2, 128, nan, 2, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_qknorm_rope(qkv, g1, g2, 1, 2, 8, 8, 2, 128, 1e-6f, nan, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn_chunk(qkv, qkv, of32, lsea, 1, 16, 16, 2, 128, nan, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn_fp8(qk8, vt8, sc, outb, nullptr, 1, 16, 2, 128, nan, &z), WAN_E_VALUE);
+  EXPECT_EQ(finite(-INFINITY), 0);
+  EXPECT_EQ(finite(3.0e38f), 1);
+
   int64_t vtb = 0;
   EXPECT_EQ(fp8_vt_bytes(2, 129, 3, &vtb), 1);
   EXPECT_EQ(vtb, 2 * 3 * 128 * 256);

@@ -85,11 +85,13 @@ def test_chunk_matches_oracle_chunk_and_full_kernel():
                                                host[b, 100:250, 2 * D + h * 128:2 * D + (h + 1) * 128], SCALE)
             assert_gates(attn_error_stats(_np(o[b, :, c]), ref), BF16_GATES, f"chunk b{b} h{h}")
             assert np.abs(_np(l[b, h]) - lref).max() <= LSE_ABS
-    # the whole sequence as one chunk is the full kernel, before its bf16 rounding
-    full_f32, _ = wan_attn.attn_fwd_chunk(qkv, qkv, heads)
-    full_bf16 = wan_attn.attn_fwd(qkv, heads)
+    # the whole sequence as one chunk is the full kernel's LSE-returning
+    # instance (both sum the fp32 probabilities), before its bf16 rounding
+    full_f32, full_l = wan_attn.attn_fwd_chunk(qkv, qkv, heads)
+    full_bf16, l16 = wan_attn.attn_fwd(qkv, heads, lse=True)
     torch.cuda.synchronize()
     assert torch.equal(full_f32.to(torch.bfloat16), full_bf16)
+    assert torch.equal(full_l, l16)
 
 
 def test_merge_into_empty_accumulator_ignores_its_contents():

@@ -151,6 +151,27 @@ def test_rope_textbook_angles():
     np.testing.assert_allclose(wan_ref.rope_apply(e, 0, 0, 2)[86:88], [-0.9092974268256817, -0.4161468365471424], rtol=1e-15)
 
 
+@pytest.mark.parametrize("band,first_pair,pairs,theta,pos_index", [
+    ("frame", 0, 22, 2.0 ** 22, 0), ("row", 22, 21, 2.0 ** 21, 1), ("column", 43, 21, 2.0 ** 21, 2)])
+def test_rope_every_pair_of_each_band(band, first_pair, pairs, theta, pos_index):
+    """Every pair of a band, not only its first: with theta = 2^22 for the
+    44-channel frame band (or 2^21 for a 42-channel band), pair j' of the band
+    has frequency 2^-j', so at position p its angle is p / 2^j' -- a closed
+    form that does not go through the theta ** (-2 j / d) expression. A wrong
+    band width, band offset or pair index within the band fails it."""
+    p = 5.0
+    pos = [1.0, 2.0, 3.0]
+    pos[pos_index] = p
+    for j in range(pairs):
+        e = np.zeros(128)
+        c = 2 * (first_pair + j)
+        e[c] = 1.0
+        out = wan_ref.rope_apply(e, pos[0], pos[1], pos[2], theta=theta)
+        ang = p / 2.0 ** j
+        np.testing.assert_allclose(out[c:c + 2], [math.cos(ang), math.sin(ang)], rtol=0, atol=1e-14,
+                                   err_msg=f"{band} band pair {j}")
+
+
 def test_rope_axis_separability():
     rng = np.random.default_rng(6)
     v = rng.standard_normal(128)

@@ -42,6 +42,43 @@ def test_bf16_midpoints_round_to_even():
     np.testing.assert_array_equal(bf16_rne(-mid), -r)
 
 
+def _bf16_code(v):
+    """Sign-magnitude 16-bit pattern of a bf16 value (via torch's cast, a library routine)."""
+    t = torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16)
+    c = t.view(torch.int16).numpy().astype(np.int64) & 0xFFFF
+    return np.where(c & 0x8000, -(c & 0x7FFF), c)  # signed magnitude order
+
+
+def test_bf16_neighbors_bracket_non_representable_values():
+    """For values that are NOT bfloat16 numbers (random fp64 of both signs,
+    bf16 subnormals, values just below and above powers of two), the two
+    neighbours are bf16 values (torch's cast leaves them unchanged), bracket x
+    strictly, are consecutive bf16 codes, and round-to-nearest picks one of
+    them. A wrong quantum (off by one exponent step) or a swapped floor/ceil
+    fails one of these."""
+    rng = np.random.default_rng(7)
+    k = rng.integers(-20, 20, 3000).astype(np.float64)
+    x = np.concatenate([
+        rng.standard_normal(50_000) * 10.0,
+        np.abs(rng.standard_normal(5_000)) * 1e-39,      # bf16 subnormal range
+        np.ldexp(1.0, k.astype(int)) * (1 - 2.0 ** -12),  # just below 2^k: quantum of the lower binade
+        np.ldexp(1.0, k.astype(int)) * (1 + 2.0 ** -10),  # just above 2^k
+        -np.ldexp(1.0, k.astype(int)) * (1 + 2.0 ** -10),
+    ])
+    x = x[bf16_rne(x) != x]                               # only non-representable values
+    lo, hi = bf16_neighbors(x)
+    assert np.all(lo < x) and np.all(x < hi)
+    np.testing.assert_array_equal(_torch_bf16(lo), lo)
+    np.testing.assert_array_equal(_torch_bf16(hi), hi)
+    np.testing.assert_array_equal(_bf16_code(hi) - _bf16_code(lo), np.ones(len(x), np.int64))
+    r = bf16_rne(x)
+    assert np.all((r == lo) | (r == hi))
+    below = np.ldexp(1.0, k.astype(int)) * (1 - 2.0 ** -12)
+    blo, bhi = bf16_neighbors(below)
+    np.testing.assert_array_equal(bhi, np.ldexp(1.0, k.astype(int)))           # the power of two itself
+    np.testing.assert_array_equal(blo, np.ldexp(1.0, k.astype(int)) * (1 - 2.0 ** -8))
+
+
 def test_bf16_overflow_and_specials():
     assert bf16_rne(np.array([BF16_MAX]))[0] == BF16_MAX
     assert np.isinf(bf16_rne(np.array([3.4e38]))[0])

@@ -35,14 +35,21 @@ def hipcc():
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-fno-honor-nans",  # max/min need no NaN canonicalisation; NaN inputs give unspecified results
             "-Wall", "-Wno-unused-command-line-argument",
             "-I", INCLUDE, "-I", CSRC]
 
 
+def kernel_flags(src):
+    """Kernel sources may assume no NaN arithmetic (max/min then need no NaN
+    canonicalisation; NaN inputs give unspecified results). The host-side
+    entry points (api.cpp) are built without that assumption, so their checks
+    of scalar arguments still see a NaN."""
+    return [] if src.endswith(".cpp") else ["-fno-honor-nans"]
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *kernel_flags(src), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -84,6 +84,21 @@ const char* wan_status_str(int status) {
   }
 }
 
+int wan_token_grid(int64_t width, int64_t height, int64_t num_frames, int64_t* T, int64_t* H, int64_t* W) {
+  if (!T || !H || !W) return WAN_E_NULL;
+  if (width < 0 || height < 0 || num_frames < 1 || (num_frames - 1) % 4 != 0) return WAN_E_SHAPE;
+  // Pixels rounded down to a multiple of 16, then 8x VAE compression and 2x
+  // patchify per spatial axis: 16 pixels per token. 4x temporal compression
+  // with the first frame kept: (F - 1) / 4 + 1 latent frames.
+  const int64_t t = (num_frames - 1) / 4 + 1, h = (height / 16) * 16 / 8 / 2, w = (width / 16) * 16 / 8 / 2;
+  int64_t hw, s;
+  if (!wan::mul_ok(h, w, &hw) || !wan::mul_ok(hw, t, &s)) return WAN_E_OVERFLOW;
+  *T = t;
+  *H = h;
+  *W = w;
+  return WAN_OK;
+}
+
 int wan_qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t B, int64_t S, int64_t heads,
                  int64_t head_dim, void* stream) {
   wan::Sizes z;

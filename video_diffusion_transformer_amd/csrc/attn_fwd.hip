@@ -35,7 +35,9 @@
 //     the transposing load, fall in distinct banks;
 //   * the O^T accumulator keeps one query column per lane, so the rescale by
 //     exp2(m_old - m_new) is lane-local, and each lane sums its own bf16
-//     probabilities (packed dot products with (1, 1)). The running max only moves when a
+//     probabilities (packed dot products with (1, 1); the instances that
+//     return a log-sum-exp sum the fp32 probabilities instead, so the LSE is
+//     exact up to fp32 rounding). The running max only moves when a
 //     tile's max exceeds it by more than 8 (log2 units): most tiles skip the
 //     rescale; the stale max keeps p <= 2^8 (exact in fp32, far from bf16
 //     overflow) and the final normalisation uses the same max, so the result is
@@ -165,49 +167,54 @@ __device__ __forceinline__ void tile_rescale(unsigned moved, const float (&alpha
 
 // p = 2^(s * scale_log2 - m) rounded to bf16, written in the B-operand layout
 // of PV (two 32-key steps per query tile: lane group g holds keys 4g..4g+3 of
-// 16-key tiles 2c and 2c+1). The row sums add up exactly these bf16 weights (a
-// dot product of each packed pair with (1, 1), fp32 sum), so the
-// normalisation matches what PV accumulated; each lane sums its own keys.
+// 16-key tiles 2c and 2c+1); each lane sums its own keys. Without ExactSum the
+// row sums add up exactly the bf16 weights PV multiplies (a dot product of each
+// packed pair with (1, 1), fp32 sum: 4 instructions per 8 weights), so the
+// normalisation matches what PV accumulated. With ExactSum they add the fp32
+// probabilities before rounding (8 adds per 8 weights), so that ln of the sum is
+// the log-sum-exp of the scores up to fp32 rounding: the instances that return
+// an LSE use it.
+template <bool ExactSum>
+__device__ __forceinline__ float exp_pack8(const TileArgs& a, const f32x4_t (&acc_s)[4][kQT], float m, int u, int c,
+                                           bf16x8_t& out, float l) {
+  const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  bf16x8_t v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float e = __builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], a.scale_log2, -m));
+    v[j] = (__bf16)e;
+    if constexpr (ExactSum) l += e;
+  }
+  out = v;
+  if constexpr (!ExactSum) {
+    // Literal shuffles: extracting the pairs through a bit cast to 32-bit
+    // lanes is miscompiled by this clang (every extraction read element 0).
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, l, false);
+  }
+  return l;
+}
+
+template <bool ExactSum>
 __device__ __forceinline__ void tile_exp(const TileArgs& a, const f32x4_t (&acc_s)[4][kQT], const float (&m_run)[kQT],
                                          bf16x8_t (&pf)[kQT][2], float (&lt)[kQT]) {
-  const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
     lt[u] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8_t v;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], a.scale_log2, -m_run[u]));
-      pf[u][c] = v;
-      // Literal shuffles: extracting the pairs through a bit cast to 32-bit
-      // lanes is miscompiled by this clang (every extraction read element 0).
-      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, lt[u], false);
-      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, lt[u], false);
-      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, lt[u], false);
-      lt[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, lt[u], false);
-    }
+    for (int c = 0; c < 2; ++c) lt[u] = exp_pack8<ExactSum>(a, acc_s, m_run[u], u, c, pf[u][c], lt[u]);
   }
 }
 
 // One query tile redone against a new running max (the rare path of tile_softmax).
+template <bool ExactSum>
 __device__ __forceinline__ void tile_exp_one(const TileArgs& a, const f32x4_t (&acc_s)[4][kQT], float m, int u,
                                              bf16x8_t (&pf)[kQT][2], float& lt) {
-  const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   lt = 0.f;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    bf16x8_t v;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[2 * c + (j >> 2)][u][j & 3], a.scale_log2, -m));
-    pf[u][c] = v;
-    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, lt, false);
-    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, lt, false);
-    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, lt, false);
-    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, lt, false);
-  }
+  for (int c = 0; c < 2; ++c) lt = exp_pack8<ExactSum>(a, acc_s, m, u, c, pf[u][c], lt);
 }
 
 // Softmax step with optimistic exponentials: all probabilities of the tile are
@@ -219,6 +226,7 @@ __device__ __forceinline__ void tile_exp_one(const TileArgs& a, const f32x4_t (&
 // query tile marked for the output rescale. Each probability is at most its
 // lane's sum, so p <= 2^slack on every kept tile: the bound a max test before
 // the exponentials gives, without computing the max where it does not move.
+template <bool ExactSum>
 __device__ __forceinline__ unsigned tile_softmax(const TileArgs& a, int k0, f32x4_t (&acc_s)[4][kQT],
                                                  float (&m_run)[kQT], float (&acc_l)[kQT], float (&alpha)[kQT],
                                                  bf16x8_t (&pf)[kQT][2]) {
@@ -234,7 +242,7 @@ __device__ __forceinline__ unsigned tile_softmax(const TileArgs& a, int k0, f32x
         }
   }
   float lt[kQT];
-  tile_exp(a, acc_s, m_run, pf, lt);
+  tile_exp<ExactSum>(a, acc_s, m_run, pf, lt);
   bool over = false;
 #pragma unroll
   for (int u = 0; u < kQT; ++u) over = over || lt[u] > kSumLimit;
@@ -257,7 +265,7 @@ __device__ __forceinline__ unsigned tile_softmax(const TileArgs& a, int k0, f32x
         m_run[u] = m_new;
         acc_l[u] *= alpha[u];
         moved |= 1u << u;
-        tile_exp_one(a, acc_s, m_new, u, pf, lt[u]);
+        tile_exp_one<ExactSum>(a, acc_s, m_new, u, pf, lt[u]);
       }
   }
 #pragma unroll
@@ -297,7 +305,7 @@ __device__ __forceinline__ void tile_pv(const TileArgs& a, const unsigned char* 
 // round with the merge in the epilogue, out16 optionally receiving a bf16 copy).
 enum OutMode { kOutBf16 = 0, kOutF32 = 1, kOutFold = 2 };
 
-template <int Mode>
+template <int Mode, bool ExactSum>
 __global__ void __launch_bounds__(kThreads, (kQT >= 4 || kWaves > 4) ? 1 : 2)
 attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ kvsrc, void* __restrict__ out,
                 float* __restrict__ lse, uint16_t* __restrict__ out16, int Sq, int S, int heads, int nqt,
@@ -388,7 +396,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // 1 copy
     }
-    const unsigned moved = tile_softmax(a, kt * kBN, acc_s, m_run, acc_l, alpha, pf);
+    const unsigned moved = tile_softmax<ExactSum>(a, kt * kBN, acc_s, m_run, acc_l, alpha, pf);
     if (moved) tile_rescale(moved, alpha, acc_o);
     // Let the next tile's direct-to-LDS writes finish before the transposed V
     // reads: measured, the PV phase runs faster without those writes competing
@@ -461,8 +469,14 @@ hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S,
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   const auto* src = static_cast<const uint16_t*>(qkv);
-  hipLaunchKernelGGL(attn_fwd_kernel<kOutBf16>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream, src,
-                     src, out, lse, nullptr, S, S, heads, nqt, scale_log2);
+  // The LSE-free instance (the attention step) normalises by the sum of the
+  // bf16 weights; the one that also returns the LSE sums the fp32 weights.
+  if (lse)
+    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
+                       stream, src, src, out, lse, nullptr, S, S, heads, nqt, scale_log2);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
+                       stream, src, src, out, nullptr, nullptr, S, S, heads, nqt, scale_log2);
   return hipGetLastError();
 }
 
@@ -472,7 +486,7 @@ hipError_t launch_attn_fwd_chunk(const void* q_src, int Sq, const void* kv_src, 
   const int64_t nblocks = (int64_t)nqt * heads * B;
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fwd_kernel<kOutF32>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<kOutF32, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), out, lse, nullptr, Sq,
                      Skv, heads, nqt, scale_log2);
   return hipGetLastError();
@@ -485,7 +499,7 @@ hipError_t launch_attn_fwd_chunk_fold(const void* q_src, int Sq, const void* kv_
   const int64_t nblocks = (int64_t)nqt * heads * B;
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fwd_kernel<kOutFold>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<kOutFold, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), acc, acc_lse,
                      static_cast<uint16_t*>(out16), Sq, Skv, heads, nqt, scale_log2);
   return hipGetLastError();

@@ -18,10 +18,13 @@
 // quantised weights used in PV.
 //
 // Work decomposition (same skeleton as the bf16 kernel):
-//   * workgroup = 4 waves = 128 queries of one (b, h); each wave owns 32 queries
-//     (two 16-column MFMA tiles);
+//   * workgroup = 8 waves = 256 queries of one (b, h), one workgroup per CU;
+//     each wave owns 32 queries (two 16-column MFMA tiles);
 //   * keys stream in units of 128 (one K = 128 MFMA step for PV) through two LDS
-//     stages, the next unit prefetched into registers during the MFMAs;
+//     stages, filled straight from global memory by global_load_lds_dwordx4 (no
+//     staging registers): the next unit is requested at the top of the
+//     iteration that consumes the current one, and one wait + barrier per unit
+//     publishes it;
 //   * S^T = K Q^T: one 16x16x128 MFMA covers all 128 channels of a 16-key tile.
 //     The K rows are fed in a permuted order -- tile t, A-row m takes key
 //     32*(m/4) + 4t + m%4 -- so that after the 8 tiles lane group g holds the
@@ -88,6 +91,10 @@ __device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// ExactSum (the instance that returns the LSE): each lane also adds up its fp32
+// probabilities before the e4m3 rounding, so the log-sum-exp is that of the
+// scores up to fp32 rounding, not of the quantised weights.
+template <bool ExactSum>
 __global__ void __launch_bounds__(kThreads, kWaves > 4 ? 1 : 2)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__ vt8,
                     const float* __restrict__ scales, uint16_t* __restrict__ out, float* __restrict__ lse, int S,
@@ -126,6 +133,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
   for (int i = 0; i < 8; ++i) acc_o[i][0] = acc_o[i][1] = f32x4_t{};
   acc_l[0] = acc_l[1] = f32x4_t{};
   float m_run[2] = {-INFINITY, -INFINITY};
+  float l32[2] = {0.f, 0.f};  // ExactSum: this lane's fp32 sum of 2^8 p
   // A operand whose row 0 is all ones (rows 1..15 zero): row 0 of ones x P^T is
   // the column sum of P, i.e. l for each query, in lane (grp 0, l16), register 0.
   const int one = l16 == 0 ? kE4m3One : 0;
@@ -210,6 +218,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
         m_run[u] = m_new;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc_l[u][i] *= alpha;
+        if constexpr (ExactSum) l32[u] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -221,6 +230,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(acc_s[t][u][i], c_log2, -m_shift));
+        if constexpr (ExactSum) l32[u] += (p[0] + p[1]) + (p[2] + p[3]);
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[u][t], false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pf[u][t] = w;
@@ -257,8 +267,14 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
         w.y = pack_bf16x2(acc_o[dt][u][2] * inv, acc_o[dt][u][3] * inv);
         *reinterpret_cast<uint2*>(op + 16 * dt) = w;
       }
-      // l8 = 2^8 * sum p, so ln(sum exp(s)) = (m + log2(l8) - 8) * ln 2
-      if (lse && grp == 0) lse[(int64_t)bh * S + q] = (m_run[u] + __log2f(l_tot) - kPLog2Scale) * 0.69314718055994531f;
+      if constexpr (ExactSum) {
+        // the four lanes of a query hold disjoint keys; their fp32 sum is
+        // 2^8 * sum p, so ln(sum exp(s)) = (m + log2(l) - 8) * ln 2
+        float l = l32[u];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (grp == 0) lse[(int64_t)bh * S + q] = (m_run[u] + __log2f(l) - kPLog2Scale) * 0.69314718055994531f;
+      }
     }
   }
 }
@@ -271,9 +287,15 @@ hipError_t launch_attn_fwd_fp8(const void* qk8, const void* vt8, const float* sc
   const int64_t nblocks = (int64_t)nqt * heads * B;
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const int S_pad = (S + 127) / 128 * 128;
-  hipLaunchKernelGGL(attn_fwd_fp8_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
-                     static_cast<const uint8_t*>(qk8), static_cast<const uint8_t*>(vt8), scales,
-                     static_cast<uint16_t*>(out), lse, S, S_pad, heads, nqt, softmax_scale);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
+                       static_cast<const uint8_t*>(qk8), static_cast<const uint8_t*>(vt8), scales,
+                       static_cast<uint16_t*>(out), lse, S, S_pad, heads, nqt, softmax_scale);
+  };
+  if (lse)
+    go(attn_fwd_fp8_kernel<true>);
+  else
+    go(attn_fwd_fp8_kernel<false>);
   return hipGetLastError();
 }
 

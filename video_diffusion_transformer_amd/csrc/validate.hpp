@@ -11,8 +11,8 @@
 // raise rather than degrade).
 #pragma once
 
-#include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "wan_attn.h"
 
@@ -30,6 +30,15 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// Finite test on the bit pattern (exponent field not all ones): unlike
+// std::isfinite it cannot be folded away by a compiler told that NaNs do not
+// occur.
+inline bool finite(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof u);
+  return (u & 0x7f800000u) != 0x7f800000u;
+}
+
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
@@ -44,6 +53,7 @@ struct Sizes {
   int64_t rows = 0;       // B*S
   int64_t qkv_elems = 0;  // B*S*3D
   int64_t out_elems = 0;  // B*S*D
+  int64_t lse_bytes = 0;  // B*heads*S*4
   bool empty = false;
 };
 
@@ -63,7 +73,7 @@ inline int check_sizes(int64_t B, int64_t S, int64_t heads, int64_t head_dim, Si
   if (!mul_ok(z->qkv_elems, 2, &t)) return WAN_E_OVERFLOW;  // bytes
   if (!mul_ok(z->rows, z->D, &z->out_elems)) return WAN_E_OVERFLOW;
   int64_t lse_elems;
-  if (!mul_ok(B * heads, S, &lse_elems)) return WAN_E_OVERFLOW;
+  if (!mul_ok(z->rows, heads, &lse_elems) || !mul_ok(lse_elems, 4, &z->lse_bytes)) return WAN_E_OVERFLOW;
   z->empty = (z->rows == 0);
   return WAN_OK;
 }
@@ -76,8 +86,8 @@ inline int validate_qknorm_rope(const void* qkv, const void* gq, const void* gk,
   if (!mul_ok(H, W, &hw) || !mul_ok(hw, T, &S)) return WAN_E_OVERFLOW;
   int rc = check_sizes(B, S, heads, head_dim, z);
   if (rc != WAN_OK) return rc;
-  if (!std::isfinite(eps) || eps < 0.f) return WAN_E_VALUE;
-  if (!std::isfinite(theta) || theta <= 0.f) return WAN_E_VALUE;
+  if (!finite(eps) || eps < 0.f) return WAN_E_VALUE;
+  if (!finite(theta) || theta <= 0.f) return WAN_E_VALUE;
   if (z->empty) return WAN_OK;
   if (!qkv || !gq || !gk) return WAN_E_NULL;
   if (!aligned(qkv, 16) || !aligned(gq, 16) || !aligned(gk, 16)) return WAN_E_ALIGN;
@@ -91,16 +101,22 @@ inline int validate_attn(const void* qkv, const void* out, const void* lse, int6
                          Sizes* z) {
   int rc = check_sizes(B, S, heads, head_dim, z);
   if (rc != WAN_OK) return rc;
-  if (!std::isfinite(scale) || scale <= 0.f) return WAN_E_VALUE;
+  if (!finite(scale) || scale <= 0.f) return WAN_E_VALUE;
   if (z->empty) return WAN_OK;
   if (!qkv || !out) return WAN_E_NULL;
   if (!aligned(qkv, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return WAN_E_ALIGN;
   const int64_t in_bytes = z->qkv_elems * in_elem_bytes, out_bytes = z->out_elems * 2;
-  const int64_t lse_bytes = z->B * z->heads * z->S * 4;
+  const int64_t lse_bytes = z->lse_bytes;
   if (overlaps(qkv, in_bytes, out, out_bytes)) return WAN_E_ALIAS;
   if (lse && (overlaps(lse, lse_bytes, qkv, in_bytes) || overlaps(lse, lse_bytes, out, out_bytes)))
     return WAN_E_ALIAS;
   return WAN_OK;
+}
+
+// Bytes of a packed bf16 [B, Skv, 3D] buffer; false on overflow.
+inline bool kv_chunk_bytes(int64_t B, int64_t Skv, int64_t D, int64_t* out) {
+  int64_t t;
+  return mul_ok(B, Skv, &t) && mul_ok(t, 3 * D, &t) && mul_ok(t, 2, out);
 }
 
 inline int validate_attn_chunk(const void* q_src, const void* kv_src, const void* out, const void* lse, int64_t B,
@@ -109,14 +125,14 @@ inline int validate_attn_chunk(const void* q_src, const void* kv_src, const void
   if (Skv > kMaxTokens) return WAN_E_OVERFLOW;
   int rc = check_sizes(B, Sq, heads, head_dim, z);
   if (rc != WAN_OK) return rc;
-  if (!std::isfinite(scale) || scale <= 0.f) return WAN_E_VALUE;
+  if (!finite(scale) || scale <= 0.f) return WAN_E_VALUE;
   if (z->empty) return WAN_OK;
   if (Skv == 0) return WAN_E_SHAPE;  // attention over no keys is undefined
   if (!q_src || !kv_src || !out || !lse) return WAN_E_NULL;
   if (!aligned(q_src, 16) || !aligned(kv_src, 16) || !aligned(out, 16) || !aligned(lse, 4)) return WAN_E_ALIGN;
   int64_t kv_elems;
-  if (!mul_ok(B * Skv, 3 * z->D, &kv_elems) || !mul_ok(kv_elems, 2, &kv_elems)) return WAN_E_OVERFLOW;
-  const int64_t q_bytes = z->qkv_elems * 2, out_bytes = z->out_elems * 4, lse_bytes = z->B * z->heads * z->S * 4;
+  if (!kv_chunk_bytes(B, Skv, z->D, &kv_elems)) return WAN_E_OVERFLOW;
+  const int64_t q_bytes = z->qkv_elems * 2, out_bytes = z->out_elems * 4, lse_bytes = z->lse_bytes;
   if (overlaps(out, out_bytes, q_src, q_bytes) || overlaps(out, out_bytes, kv_src, kv_elems) ||
       overlaps(lse, lse_bytes, q_src, q_bytes) || overlaps(lse, lse_bytes, kv_src, kv_elems) ||
       overlaps(lse, lse_bytes, out, out_bytes))
@@ -133,7 +149,7 @@ inline int validate_attn_merge(const void* acc, const void* acc_lse, const void*
   if (!aligned(acc, 16) || !aligned(chunk, 16) || !aligned(acc_lse, 4) || !aligned(chunk_lse, 4) ||
       (out16 && !aligned(out16, 16)))
     return WAN_E_ALIGN;
-  const int64_t o_bytes = z->out_elems * 4, l_bytes = z->B * z->heads * z->S * 4, h_bytes = z->out_elems * 2;
+  const int64_t o_bytes = z->out_elems * 4, l_bytes = z->lse_bytes, h_bytes = z->out_elems * 2;
   const void* p[5] = {acc, acc_lse, chunk, chunk_lse, out16};
   const int64_t n[5] = {o_bytes, l_bytes, o_bytes, l_bytes, h_bytes};
   for (int i = 0; i < 5; ++i)
@@ -151,11 +167,10 @@ inline int validate_attn_chunk_fold(const void* q_src, const void* kv_src, const
   if (rc != WAN_OK || z->empty) return rc;
   if (out16 && !aligned(out16, 16)) return WAN_E_ALIGN;
   int64_t kv_bytes;
-  mul_ok(B * Skv, 3 * z->D, &kv_bytes);
-  kv_bytes *= 2;
+  if (!kv_chunk_bytes(B, Skv, z->D, &kv_bytes)) return WAN_E_OVERFLOW;
   const int64_t h_bytes = z->out_elems * 2;
   if (overlaps(out16, h_bytes, q_src, z->qkv_elems * 2) || overlaps(out16, h_bytes, kv_src, kv_bytes) ||
-      overlaps(out16, h_bytes, acc, z->out_elems * 4) || overlaps(out16, h_bytes, acc_lse, z->B * z->heads * z->S * 4))
+      overlaps(out16, h_bytes, acc, z->out_elems * 4) || overlaps(out16, h_bytes, acc_lse, z->lse_bytes))
     return WAN_E_ALIAS;
   return WAN_OK;
 }
@@ -178,6 +193,7 @@ inline int validate_qkv_proj(const void* x, const void* w, const void* bias, con
 
 // Bytes of the transposed fp8 V buffer: B * heads * 128 * S_pad, S_pad = S rounded up to 128.
 inline bool fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t* out) {
+  if (S < 0 || S > INT64_MAX - 127) return false;
   const int64_t s_pad = (S + 127) / 128 * 128;
   int64_t t;
   return mul_ok(B, heads, &t) && mul_ok(t, kHeadDim, &t) && mul_ok(t, s_pad, out);
@@ -218,7 +234,7 @@ inline int validate_qknorm_rope_fp8(const void* qkv, const void* gq, const void*
   rc = validate_quant_fp8(qkv, qk8, vt8, scales, amax, B, z->S, heads, head_dim, z);
   if (rc != WAN_OK || z->empty) return rc;
   int64_t vt_bytes;
-  fp8_vt_bytes(B, z->S, heads, &vt_bytes);
+  if (!fp8_vt_bytes(B, z->S, heads, &vt_bytes)) return WAN_E_OVERFLOW;
   const void* outs[4] = {qk8, vt8, scales, amax};
   const int64_t sizes[4] = {z->rows * 2 * z->D, vt_bytes, 12, 12};
   for (int i = 0; i < 4; ++i)
@@ -231,7 +247,7 @@ inline int validate_attn_fp8(const void* qk8, const void* vt8, const void* scale
                              Sizes* z) {
   int rc = check_sizes(B, S, heads, head_dim, z);
   if (rc != WAN_OK) return rc;
-  if (!std::isfinite(scale) || scale <= 0.f) return WAN_E_VALUE;
+  if (!finite(scale) || scale <= 0.f) return WAN_E_VALUE;
   if (z->empty) return WAN_OK;
   if (!qk8 || !vt8 || !scales || !out) return WAN_E_NULL;
   if (!aligned(qk8, 16) || !aligned(vt8, 16) || !aligned(scales, 4) || !aligned(out, 16) ||
@@ -239,7 +255,7 @@ inline int validate_attn_fp8(const void* qk8, const void* vt8, const void* scale
     return WAN_E_ALIGN;
   int64_t vt_bytes;
   if (!fp8_vt_bytes(B, S, heads, &vt_bytes)) return WAN_E_OVERFLOW;
-  const int64_t qk_bytes = z->rows * 2 * z->D, out_bytes = z->out_elems * 2, lse_bytes = z->B * z->heads * z->S * 4;
+  const int64_t qk_bytes = z->rows * 2 * z->D, out_bytes = z->out_elems * 2, lse_bytes = z->lse_bytes;
   const void* ins[3] = {qk8, vt8, scales};
   const int64_t in_sizes[3] = {qk_bytes, vt_bytes, 12};
   for (int i = 0; i < 3; ++i) {

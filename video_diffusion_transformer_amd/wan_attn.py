@@ -5,9 +5,10 @@ kernels behind the C ABI declared in include/wan_attn.h. Tensors must already
 live on the GPU; there is no CPU path. If the library is not built the first
 call raises -- nothing falls back to another implementation.
 
-The names follow the C ABI: ``qkv_proj`` -> wan_qkv_proj, ``qknorm_rope`` -> wan_qknorm_rope,
-``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_chunk`` -> wan_attn_fwd_chunk,
-``attn_merge`` -> wan_attn_merge, ``attn_fwd_chunk_merge`` -> wan_attn_fwd_chunk_merge,
+The names follow the C ABI: ``token_grid`` -> wan_token_grid, ``qkv_proj`` -> wan_qkv_proj,
+``qknorm_rope`` -> wan_qknorm_rope, ``attn_fwd`` -> wan_attn_fwd,
+``attn_fwd_chunk`` -> wan_attn_fwd_chunk, ``attn_merge`` -> wan_attn_merge,
+``attn_fwd_chunk_merge`` -> wan_attn_fwd_chunk_merge,
 ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
 ``qknorm_rope_quant_fp8`` -> wan_qknorm_rope_quant_fp8, ``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
 """
@@ -35,6 +36,8 @@ _P, _I64, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
 SIGNATURES = {
     "wan_abi_version": (ctypes.c_int, []),
     "wan_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "wan_token_grid": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                                      ctypes.POINTER(_I64)]),
     "wan_qkv_proj": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
@@ -98,15 +101,12 @@ def _need_gpu(name, t, dtype):
 
 
 def token_grid(width, height, num_frames):
-    """(T, H, W) token grid of a clip: height and width rounded down to a
-    multiple of 16, 8x spatial / 4x temporal VAE compression, 2x2 patchify
-    ("Optimizing High-Quality Offline Video Generation", Grounding in an output
-    spec)."""
-    if num_frames < 1 or (num_frames - 1) % 4:
-        raise ValueError("num_frames must be 4k+1")
-    w = (width // 16) * 16 // 8 // 2
-    h = (height // 16) * 16 // 8 // 2
-    return (num_frames - 1) // 4 + 1, h, w
+    """(T, H, W) token grid of a clip of width x height pixels and num_frames
+    frames, from wan_token_grid. Raises WanError on invalid sizes."""
+    T, H, W = _I64(), _I64(), _I64()
+    _check("wan_token_grid", lib().wan_token_grid(width, height, num_frames, ctypes.byref(T), ctypes.byref(H),
+                                                  ctypes.byref(W)))
+    return T.value, H.value, W.value
 
 
 def qkv_proj(x, w_qkv, heads, bias=None, head_dim=HEAD_DIM, out=None, stream=None):
@@ -275,6 +275,38 @@ class Fp8QKV:
         return (self.S + 127) // 128 * 128
 
 
+def check_fp8_buffers(f, B, S, heads, head_dim=HEAD_DIM):
+    """Sizes of the buffers of an Fp8QKV against (B, S, heads): the C ABI cannot
+    see buffer sizes, so a short or mismatched buffer is refused here. Checks
+    shapes and dtypes only (works on tensors of any device)."""
+    D = heads * head_dim
+    if (f.B, f.S, f.heads) != (B, S, heads):
+        raise ValueError(f"fp8 buffers are for (B, S, heads) = {(f.B, f.S, f.heads)}, not {(B, S, heads)}")
+    for name, t, dt in (("qk8", f.qk8, torch.uint8), ("vt8", f.vt8, torch.uint8), ("scales", f.scales, torch.float32),
+                        ("amax", f.amax, torch.float32)):
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if f.qk8.numel() != B * S * 2 * D:
+        raise ValueError(f"qk8 must hold B*S*2*D = {B * S * 2 * D} bytes, got {f.qk8.numel()}")
+    vt_need = lib().wan_fp8_vt_bytes(B, S, heads, head_dim)
+    if vt_need < 0 or f.vt8.numel() < vt_need:
+        raise ValueError(f"vt8 must hold {vt_need} bytes, got {f.vt8.numel()}")
+    if f.scales.numel() != 3 or f.amax.numel() != 3:
+        raise ValueError("scales and amax must hold 3 floats each")
+
+
+def check_attn_outputs(out, lse, B, S, heads, head_dim=HEAD_DIM):
+    """out must be a contiguous bf16 [B, S, D] tensor and lse (if not None) a
+    contiguous fp32 [B, heads, S] one; shapes and dtypes only."""
+    D = heads * head_dim
+    if not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16 or tuple(out.shape) != (B, S, D) \
+            or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 tensor of shape {(B, S, D)}")
+    if lse is not None and (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+                            or tuple(lse.shape) != (B, heads, S) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous fp32 tensor of shape {(B, heads, S)}")
+
+
 def fp8_buffers(B, S, heads, device, head_dim=HEAD_DIM):
     """Allocate the buffers qkv_quant_fp8 writes."""
     D = heads * head_dim
@@ -295,12 +327,11 @@ def qkv_quant_fp8(qkv, heads, head_dim=HEAD_DIM, out=None, stream=None):
     if qkv.dim() != 3 or qkv.shape[2] != 3 * heads * head_dim:
         raise ValueError("qkv must be [B, S, 3*heads*head_dim]")
     f = out if out is not None else fp8_buffers(B, S, heads, qkv.device, head_dim)
+    check_fp8_buffers(f, B, S, heads, head_dim)
     for name in ("qk8", "vt8"):
         _need_gpu(name, getattr(f, name), torch.uint8)
     _need_gpu("scales", f.scales, torch.float32)
     _need_gpu("amax", f.amax, torch.float32)
-    if f.vt8.numel() < lib().wan_fp8_vt_bytes(B, S, heads, head_dim) or f.qk8.numel() != B * S * 2 * heads * head_dim:
-        raise ValueError("fp8 buffers are too small for these sizes")
     with torch.cuda.device(qkv.device):
         _check("wan_qkv_quant_fp8", lib().wan_qkv_quant_fp8(
             _ptr(qkv), _ptr(f.qk8), _ptr(f.vt8), _ptr(f.scales), _ptr(f.amax), B, S, heads, head_dim,
@@ -323,12 +354,11 @@ def qknorm_rope_quant_fp8(qkv, gamma_q, gamma_k, grid, heads, head_dim=HEAD_DIM,
     if gamma_q.numel() != D or gamma_k.numel() != D:
         raise ValueError("gammas must have heads*head_dim elements")
     f = out if out is not None else fp8_buffers(B, S, heads, qkv.device, head_dim)
+    check_fp8_buffers(f, B, S, heads, head_dim)
     for name in ("qk8", "vt8"):
         _need_gpu(name, getattr(f, name), torch.uint8)
     _need_gpu("scales", f.scales, torch.float32)
     _need_gpu("amax", f.amax, torch.float32)
-    if f.vt8.numel() < lib().wan_fp8_vt_bytes(B, S, heads, head_dim) or f.qk8.numel() != B * S * 2 * D:
-        raise ValueError("fp8 buffers are too small for these sizes")
     with torch.cuda.device(qkv.device):
         _check("wan_qknorm_rope_quant_fp8", lib().wan_qknorm_rope_quant_fp8(
             _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), B, T, H, W, heads, head_dim, eps, theta,
@@ -340,14 +370,19 @@ def attn_fwd_fp8(f, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=False, 
     """Attention from an Fp8QKV. Returns out [B, S, D] bf16 (and lse)."""
     B, S, heads = f.B, f.S, f.heads
     D = heads * head_dim
+    check_fp8_buffers(f, B, S, heads, head_dim)
     scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else float(softmax_scale)
     dev = f.qk8.device
     if out is None:
         out = torch.empty((B, S, D), dtype=torch.bfloat16, device=dev)
-    _need_gpu("out", out, torch.bfloat16)
     want_lse = lse is not False and lse is not None
     if lse is True:
         lse = torch.empty((B, heads, S), dtype=torch.float32, device=dev)
+    check_attn_outputs(out, lse if want_lse else None, B, S, heads, head_dim)
+    for name in ("qk8", "vt8"):
+        _need_gpu(name, getattr(f, name), torch.uint8)
+    _need_gpu("scales", f.scales, torch.float32)
+    _need_gpu("out", out, torch.bfloat16)
     if want_lse:
         _need_gpu("lse", lse, torch.float32)
     with torch.cuda.device(dev):
