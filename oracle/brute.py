@@ -65,3 +65,31 @@ def linear_brute(x, w, bias=None):
             row.append(math.fsum(terms))
         out.append(row)
     return out
+
+
+def attention_skip_brute(q, k, v, scale, threshold, block_q, block_k):
+    """Skip-Softmax threshold mode with scalar loops: running maximum over the
+    key blocks in order, the per-query-block decision with math.exp, then the
+    softmax over the kept keys with exact summation. Returns (o, lse, kept)."""
+    M, N = len(q), len(k)
+    s = [[scale * math.fsum(qi[c] * kj[c] for c in range(len(qi))) for kj in k] for qi in q]
+    nqb, nkb = (M + block_q - 1) // block_q, (N + block_k - 1) // block_k
+    kept = [[True] * nkb for _ in range(nqb)]
+    prev = [-math.inf] * M
+    for j in range(nkb):
+        keys = range(j * block_k, min(N, (j + 1) * block_k))
+        bmax = [max(s[i][t] for t in keys) for i in range(M)]
+        for b in range(nqb):
+            rows = range(b * block_q, min(M, (b + 1) * block_q))
+            if j > 0 and all(math.exp(bmax[i] - prev[i]) < threshold for i in rows):
+                kept[b][j] = False
+        prev = [max(prev[i], bmax[i]) for i in range(M)]
+    o, lse = [], []
+    for i in range(M):
+        use = [t for t in range(N) if kept[i // block_q][t // block_k]]
+        m = max(s[i][t] for t in use)
+        p = {t: math.exp(s[i][t] - m) for t in use}
+        den = math.fsum(p.values())
+        o.append([math.fsum(p[t] * v[t][c] for t in use) / den for c in range(len(v[0]))])
+        lse.append(m + math.log(den))
+    return o, lse, kept

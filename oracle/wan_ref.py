@@ -14,6 +14,8 @@ Sources (web pages on Wan2.2; cited by title and section):
        (40 heads x 128 channels, hidden 5120).
   [P4] "Wan2.2-A14B" (TT-DiT model notes), section "Details": each block has
        self-attention with RoPE positional embeddings.
+  [P2] "Wan2.2 Text-to-Video" (vLLM-Omni recipe), section "Accelerating
+       with TRTLLM_ATTN + Skip-Softmax": the Skip-Softmax threshold mode.
   [P5] "[visual_gen] Optimize Wan2.2 Dataflow" (TensorRT-LLM pull request):
        change 1 (Q and K read as strided views of one fused QKV allocation,
        [Q | K | V] layout kept, updated in place); "Numerical Behavior ->
@@ -36,6 +38,9 @@ Readings where the pages are silent (each is listed in the design notes):
   * Attention scale is 1/sqrt(head_dim); no mask; the log-sum-exp is natural.
   * fp8: one scale per tensor (Q, K, V), scale = fl32(448 / amax), computed
     after norm and RoPE; an all-zero tensor gets scale 1.
+  * Skip-Softmax threshold mode: a key block is skipped for a query block when
+    no row of it has exp(block max - max of all earlier blocks) >= threshold
+    (``skip_blocks_ref``); keys in increasing order, fixed block sizes.
 """
 
 import numpy as np
@@ -217,6 +222,67 @@ def lse_merge_ref(o_a, lse_a, o_b, lse_b):
     wa = np.exp(lse_a - lse)[..., None]
     wb = np.exp(lse_b - lse)[..., None]
     return wa * o_a + wb * o_b, lse
+
+
+# --------------------------------------------------------------------------
+# Skip-Softmax, threshold mode   ([P2] "Accelerating with TRTLLM_ATTN +
+# Skip-Softmax", table "Skip-Softmax controls": ``threshold`` is a direct skip
+# threshold, finite and >= 0, needing no calibration)
+# --------------------------------------------------------------------------
+def skip_blocks_ref(s, threshold, block_q, block_k):
+    """Which (query block, key block) pairs the threshold rule keeps.
+
+    The page names the knob, not the rule; the reading taken here: keys are
+    processed in blocks of ``block_k`` consecutive keys in increasing order,
+    queries in blocks of ``block_q`` consecutive rows. For query row i and key
+    block j, let m_j(i) be the largest score of the block and M_j(i) the
+    largest score of all earlier blocks (-inf for j = 0). The block's
+    softmax (and its product with V) is skipped for a query block when
+    exp(m_j(i) - M_j(i)) < threshold for EVERY row i of the query block, i.e.
+    no row can gain from it more than ``threshold`` relative to the best key
+    already seen. threshold = 0 keeps everything; block 0 is always kept.
+
+    s: [M, N] fp64 scores (already scaled). Returns (kept [nqb, nkb] bool,
+    margin [nqb, nkb]): margin = |max_i (m_j(i) - M_j(i)) - ln threshold|, the
+    distance of the deciding quantity from the threshold (inf where nothing
+    is decided: threshold 0, block 0)."""
+    M, N = s.shape
+    nqb, nkb = -(-M // block_q), -(-N // block_k)
+    blockmax = np.stack([s[:, j * block_k:(j + 1) * block_k].max(axis=1) for j in range(nkb)])  # [nkb, M]
+    prev = np.full(M, -np.inf)
+    kept = np.ones((nqb, nkb), bool)
+    margin = np.full((nqb, nkb), np.inf)
+    for j in range(nkb):
+        d = blockmax[j] - prev  # +inf for block 0
+        for b in range(nqb):
+            dmax = d[b * block_q:(b + 1) * block_q].max()
+            with np.errstate(over="ignore"):
+                kept[b, j] = not (np.exp(dmax) < threshold)
+            if threshold > 0 and np.isfinite(dmax):
+                margin[b, j] = abs(dmax - np.log(threshold))
+        prev = np.maximum(prev, blockmax[j])
+    return kept, margin
+
+
+def attention_skip_ref(q, k, v, scale, threshold, block_q, block_k, kept=None):
+    """Attention of one head with Skip-Softmax in threshold mode: softmax over
+    the keys of the kept blocks only (a skipped block adds nothing to the
+    numerator or the denominator), the rule of ``skip_blocks_ref``.
+
+    ``kept`` may be given to impose the block decisions (used where a decision
+    lies within rounding of the threshold and both outcomes are correct).
+    Returns (o, lse, kept, margin); lse is over the kept keys."""
+    s = (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T) * scale
+    k_kept, margin = skip_blocks_ref(s, threshold, block_q, block_k)
+    kept = k_kept if kept is None else np.asarray(kept, bool)
+    M, N = s.shape
+    mask = np.repeat(np.repeat(kept, block_q, axis=0)[:M], block_k, axis=1)[:, :N]
+    sm = np.where(mask, s, -np.inf)
+    m = sm.max(axis=1, keepdims=True)
+    p = np.exp(sm - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ np.asarray(v, np.float64)) / l
+    return o, m[:, 0] + np.log(l[:, 0]), kept, margin
 
 
 # --------------------------------------------------------------------------
