@@ -68,22 +68,24 @@ def linear_brute(x, w, bias=None):
 
 
 def attention_skip_brute(q, k, v, scale, threshold, block_q, block_k):
-    """Skip-Softmax threshold mode with scalar loops: running maximum over the
-    key blocks in order, the per-query-block decision with math.exp, then the
+    """Skip-Softmax threshold mode with scalar loops: running maximum of the
+    kept key blocks in order, the per-query-block decision with math.exp, then the
     softmax over the kept keys with exact summation. Returns (o, lse, kept)."""
     M, N = len(q), len(k)
     s = [[scale * math.fsum(qi[c] * kj[c] for c in range(len(qi))) for kj in k] for qi in q]
     nqb, nkb = (M + block_q - 1) // block_q, (N + block_k - 1) // block_k
     kept = [[True] * nkb for _ in range(nqb)]
-    prev = [-math.inf] * M
+    run = [-math.inf] * M  # running max of the kept blocks
     for j in range(nkb):
         keys = range(j * block_k, min(N, (j + 1) * block_k))
         bmax = [max(s[i][t] for t in keys) for i in range(M)]
         for b in range(nqb):
             rows = range(b * block_q, min(M, (b + 1) * block_q))
-            if j > 0 and all(math.exp(bmax[i] - prev[i]) < threshold for i in rows):
+            if j > 0 and all(math.exp(bmax[i] - run[i]) < threshold for i in rows):
                 kept[b][j] = False
-        prev = [max(prev[i], bmax[i]) for i in range(M)]
+            else:
+                for i in rows:
+                    run[i] = max(run[i], bmax[i])
     o, lse = [], []
     for i in range(M):
         use = [t for t in range(N) if kept[i // block_q][t // block_k]]

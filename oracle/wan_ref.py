@@ -39,8 +39,9 @@ Readings where the pages are silent (each is listed in the design notes):
   * fp8: one scale per tensor (Q, K, V), scale = fl32(448 / amax), computed
     after norm and RoPE; an all-zero tensor gets scale 1.
   * Skip-Softmax threshold mode: a key block is skipped for a query block when
-    no row of it has exp(block max - max of all earlier blocks) >= threshold
-    (``skip_blocks_ref``); keys in increasing order, fixed block sizes.
+    no row of it has exp(block max - running max of the kept blocks) >=
+    threshold (``skip_blocks_ref``); keys in increasing order, fixed block
+    sizes.
 """
 
 import numpy as np
@@ -236,11 +237,14 @@ def skip_blocks_ref(s, threshold, block_q, block_k):
     processed in blocks of ``block_k`` consecutive keys in increasing order,
     queries in blocks of ``block_q`` consecutive rows. For query row i and key
     block j, let m_j(i) be the largest score of the block and M_j(i) the
-    largest score of all earlier blocks (-inf for j = 0). The block's
+    running maximum of the softmax before it: the largest score of the
+    earlier blocks KEPT for i's query block (-inf for j = 0). The block's
     softmax (and its product with V) is skipped for a query block when
     exp(m_j(i) - M_j(i)) < threshold for EVERY row i of the query block, i.e.
     no row can gain from it more than ``threshold`` relative to the best key
-    already seen. threshold = 0 keeps everything; block 0 is always kept.
+    it has used so far. threshold = 0 keeps everything; block 0 is always kept.
+    (For threshold <= 1 a skipped block never holds a new maximum, so M_j is
+    also the largest score of all earlier blocks.)
 
     s: [M, N] fp64 scores (already scaled). Returns (kept [nqb, nkb] bool,
     margin [nqb, nkb]): margin = |max_i (m_j(i) - M_j(i)) - ln threshold|, the
@@ -249,18 +253,20 @@ def skip_blocks_ref(s, threshold, block_q, block_k):
     M, N = s.shape
     nqb, nkb = -(-M // block_q), -(-N // block_k)
     blockmax = np.stack([s[:, j * block_k:(j + 1) * block_k].max(axis=1) for j in range(nkb)])  # [nkb, M]
-    prev = np.full(M, -np.inf)
+    run = np.full(M, -np.inf)  # running max of the kept blocks, per row
     kept = np.ones((nqb, nkb), bool)
     margin = np.full((nqb, nkb), np.inf)
     for j in range(nkb):
-        d = blockmax[j] - prev  # +inf for block 0
+        d = blockmax[j] - run  # +inf for block 0
         for b in range(nqb):
-            dmax = d[b * block_q:(b + 1) * block_q].max()
+            rows = slice(b * block_q, (b + 1) * block_q)
+            dmax = d[rows].max()
             with np.errstate(over="ignore"):
                 kept[b, j] = not (np.exp(dmax) < threshold)
             if threshold > 0 and np.isfinite(dmax):
                 margin[b, j] = abs(dmax - np.log(threshold))
-        prev = np.maximum(prev, blockmax[j])
+            if kept[b, j]:
+                run[rows] = np.maximum(run[rows], blockmax[j][rows])
     return kept, margin
 
 

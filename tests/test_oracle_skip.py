@@ -47,13 +47,15 @@ def _scores_case():
 
 
 def test_hand_built_skipped_sets():
-    """Row 0 has block maxima 5, 1, 6, 5.9 against earlier maxima -inf, 5, 5,
+    """Row 0 has block maxima 5, 1, 6, 5.9 against running maxima -inf, 5, 5,
     6: d = inf, -4, 1, -0.1. Row 1: maxima 0, 3, 1, 2 against -inf, 0, 3, 3:
     d = inf, 3, -2, -1. With one query per block, threshold 0.02 skips only
     (row 0, block 1) (exp(-4) = 0.0183); threshold 0.5 also skips (row 1,
     block 2) (exp(-2) = 0.135) and (row 1, block 3) (exp(-1) = 0.368); and
     threshold 1 adds (row 0, block 3) (exp(-0.1) = 0.905). With both rows in
-    one query block a block is skipped only if skipped for both rows."""
+    one query block a block is skipped only if skipped for both rows (here
+    every kept block moves the running max only where the rows agree, so the
+    joint decision is the OR of the two rows')."""
     q, k, v, s = _scores_case()
     exp = {0.02: [[1, 0, 1, 1], [1, 1, 1, 1]],
            0.5: [[1, 0, 1, 1], [1, 1, 0, 0]],
@@ -120,6 +122,18 @@ def test_skipped_set_grows_with_the_threshold():
             assert np.all(kept <= prev), tau
         prev = kept
     assert not prev.all()
+
+
+def test_running_max_is_that_of_the_kept_blocks():
+    """A threshold above 1 can skip a block that holds a new maximum; the
+    running max then stays at the kept blocks' maximum, so a later block is
+    judged against that. Scores (one query, block_k = 1): 0, 0.5, 0.9. With
+    threshold 2 (ln 2 = 0.693): block 1 has d = 0.5 < 0.693 -> skipped, the
+    running max stays 0; block 2 has d = 0.9 -> kept. (Judged against the max
+    of all earlier blocks, 0.5, block 2 would have d = 0.4 and be skipped.)"""
+    s = np.array([[0.0, 0.5, 0.9]])
+    kept, _ = wan_ref.skip_blocks_ref(s, 2.0, 1, 1)
+    np.testing.assert_array_equal(kept, [[True, False, True]])
 
 
 def test_imposed_decisions_are_used():
