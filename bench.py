@@ -27,6 +27,10 @@ timed steps. One JSON line is printed.
   cpu_baseline the fp64 numpy oracle on the host cores: attention on a bounded
               sample (query rows of one head against all keys) and the norm +
               RoPE over the full 480p tensor.
+  skip_softmax (bf16 workloads) Skip-Softmax attention (threshold mode)
+              against dense attention on a local-score input of the same
+              shape: skipped fraction of the (query block, key block) pairs,
+              both times and the speedup; not part of the step or of value.
   ring_share  (bf16 workloads) one GPU's share of ring attention with the
               sequence split over --ring-cp ranks: S/cp queries against cp
               K/V chunks, each round folded into the accumulator by the
@@ -226,6 +230,47 @@ def qkv_proj(w, dev, reps=3):
             "traffic": committed_traffic("qkv_proj", w.name)}
 
 
+def skip_softmax(w, dev, threshold, reps=3):
+    """Skip-Softmax (threshold mode) against dense attention on the same
+    input: the seeded local-score buffer of the workload's shape (scores fall
+    off with 3-D grid distance; Q and K already at unit RMS, i.e. the attention
+    input). HIP events on the stream, reps calls each after one warm-up; the
+    skipped fraction comes from one more call that writes the decision map."""
+    import torch
+
+    from video_diffusion_transformer_amd import synth, wan_attn
+
+    if threshold <= 0 or w.dtype != "bf16":
+        return None
+    qkv = synth.make_qkv_local(w.B, w.T, w.H, w.W, w.heads, seed=w.seed).to(dev)
+    out = torch.empty((w.B, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    dense = timed(lambda: wan_attn.attn_fwd(qkv, w.heads, out=out))
+    skip = timed(lambda: wan_attn.attn_fwd_skip(qkv, w.heads, threshold, out=out))
+    _, kept = wan_attn.attn_fwd_skip(qkv, w.heads, threshold, out=out, kept=True)
+    frac = 1.0 - kept.float().mean().item()
+    del qkv, out, kept
+    flop = w.attn_flop()
+    return {"threshold": threshold, "skipped_fraction": round(frac, 4), "ms_dense": round(dense, 4),
+            "ms_skip": round(skip, 4), "speedup": round(dense / skip, 3),
+            "dense_equivalent_tflops": round(flop / (skip * 1e-3) / 1e12, 2),
+            "input": "local scores: per (b, h) random Fourier features of the token's 3-D grid position "
+                     "(length 2 tokens) plus 0.3 N(0, 1) noise, q.k/sqrt(128) about 12 at distance 0; "
+                     f"{w.name} shape"}
+
+
 def run_steps(w, dev, steps, warmup, fp8_unfused=False):
     """Allocate the workload's buffers and run warm-up + timed steps. Returns
     (timings, qkv) with per-step means in ms of the step and of its phases."""
@@ -322,6 +367,9 @@ def main():
                          "(bf16 workloads; 0 to skip)")
     ap.add_argument("--proj-reps", type=int, default=3, metavar="N",
                     help="timed calls of the QKV projection on the workload's tokens (bf16 workloads; 0 to skip)")
+    ap.add_argument("--skip-threshold", type=float, default=0.02, metavar="T",
+                    help="also time Skip-Softmax attention at this threshold against dense attention on a "
+                         "local-score input of the workload's shape (bf16 workloads; 0 to skip)")
     ap.add_argument("--config-steps", type=int, default=5, metavar="N",
                     help="timed steps of each other workload (720p, 720p_fp8, long) reported next to the 480p "
                          "headline; 0 to skip them")
@@ -381,6 +429,11 @@ def main():
     proj = qkv_proj(w, dev, args.proj_reps)
     if proj:
         rec["qkv_proj"] = proj
+    torch.cuda.empty_cache()
+    sk = skip_softmax(w, dev, args.skip_threshold)
+    if sk:
+        rec["skip_softmax"] = sk
+        torch.cuda.empty_cache()
     if args.workload == "480p" and args.config_steps > 0:
         for name in EXTRA_WORKLOADS:
             x = WORKLOADS[name]

@@ -196,6 +196,45 @@ int wan_attn_fwd(const void *qkv, void *out, float *lse,
                  float softmax_scale, void *stream);
 
 /*
+ * wan_attn_fwd_skip -- wan_attn_fwd with Skip-Softmax in threshold mode (the
+ * vLLM-Omni recipe "Wan2.2 Text-to-Video", section "Accelerating with
+ * TRTLLM_ATTN + Skip-Softmax", table "Skip-Softmax controls": `threshold` is a
+ * direct skip threshold, finite and >= 0, calibration-free; the mode does not
+ * apply to ring sequence parallelism, so there is no chunk variant).
+ *
+ * The page defines the knob, not the rule; the rule implemented: keys are
+ * taken in blocks of WAN_SKIP_BLOCK_K consecutive keys in increasing order and
+ * queries in blocks of WAN_SKIP_BLOCK_Q consecutive rows (from key 0 and row 0
+ * of each (b, head)). For query row i and key block j, let m_j(i) be the
+ * block's largest score and M_j(i) the largest score of all earlier blocks
+ * (-inf for j = 0). Block j is skipped for a query block when
+ *   exp(m_j(i) - M_j(i)) < threshold   for every row i of the query block;
+ * a skipped block contributes neither to the softmax numerator nor to its
+ * denominator. Block 0 is always kept; threshold = 0 is dense attention. The
+ * scores of every block are computed; only the softmax and PV of a skipped
+ * block are not.
+ *
+ *   qkv, out, lse, B, S, heads, head_dim, softmax_scale: as wan_attn_fwd
+ *              (lse, when given, is over the kept keys).
+ *   kept       uint8 [B, heads, ceil(S / WAN_SKIP_BLOCK_Q), ceil(S / WAN_SKIP_BLOCK_K)]
+ *              decision map (1 = the block was kept for that query block), or
+ *              NULL; size from wan_attn_skip_map_bytes(). Must not overlap
+ *              the other buffers.
+ *   threshold  finite, >= 0.
+ * Errors: as wan_attn_fwd; WAN_E_VALUE also for a negative or non-finite
+ * threshold.
+ */
+#define WAN_SKIP_BLOCK_Q 48
+#define WAN_SKIP_BLOCK_K 64
+int wan_attn_fwd_skip(const void *qkv, void *out, float *lse, uint8_t *kept,
+                      int64_t B, int64_t S, int64_t heads, int64_t head_dim,
+                      float softmax_scale, float threshold, void *stream);
+
+/* Bytes of the decision map of wan_attn_fwd_skip; -1 on invalid sizes or
+ * overflow. Pure host arithmetic. */
+int64_t wan_attn_skip_map_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim);
+
+/*
  * wan_attn_fwd_chunk -- one round of ring attention on one device ("Optimizing
  * High-Quality Offline Video Generation", Context parallelism: each rank keeps
  * its S/CP queries and K/V chunks rotate around the ring so the local queries

@@ -230,7 +230,7 @@ def lse_merge_ref(o_a, lse_a, o_b, lse_b):
 # Skip-Softmax", table "Skip-Softmax controls": ``threshold`` is a direct skip
 # threshold, finite and >= 0, needing no calibration)
 # --------------------------------------------------------------------------
-def skip_blocks_ref(s, threshold, block_q, block_k):
+def skip_blocks_ref(s, threshold, block_q, block_k, history=None):
     """Which (query block, key block) pairs the threshold rule keeps.
 
     The page names the knob, not the rule; the reading taken here: keys are
@@ -249,7 +249,13 @@ def skip_blocks_ref(s, threshold, block_q, block_k):
     s: [M, N] fp64 scores (already scaled). Returns (kept [nqb, nkb] bool,
     margin [nqb, nkb]): margin = |max_i (m_j(i) - M_j(i)) - ln threshold|, the
     distance of the deciding quantity from the threshold (inf where nothing
-    is decided: threshold 0, block 0)."""
+    is decided: threshold 0, block 0).
+
+    history: optional [nqb, nkb] decisions to carry the running max with
+    instead of the rule's own (each block is still judged by the rule, given
+    that history): where a decision lies within rounding of the threshold
+    either outcome is correct, and the later blocks are then judged against
+    the running max the other outcome leaves."""
     M, N = s.shape
     nqb, nkb = -(-M // block_q), -(-N // block_k)
     blockmax = np.stack([s[:, j * block_k:(j + 1) * block_k].max(axis=1) for j in range(nkb)])  # [nkb, M]
@@ -265,7 +271,7 @@ def skip_blocks_ref(s, threshold, block_q, block_k):
                 kept[b, j] = not (np.exp(dmax) < threshold)
             if threshold > 0 and np.isfinite(dmax):
                 margin[b, j] = abs(dmax - np.log(threshold))
-            if kept[b, j]:
+            if (kept[b, j] if history is None else history[b, j]):
                 run[rows] = np.maximum(run[rows], blockmax[j][rows])
     return kept, margin
 

@@ -168,6 +168,24 @@ int main() {
   EXPECT_EQ(finite(-INFINITY), 0);
   EXPECT_EQ(finite(3.0e38f), 1);
 
+  // Skip-Softmax: the attention checks, a finite threshold >= 0, and a
+  // decision map distinct from the other buffers
+  alignas(16) static unsigned char mapb[4096];
+  EXPECT_EQ(validate_attn_skip(qkv, outb, lseb, mapb, 1, 16, 2, 128, 0.088f, 0.02f, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_skip(qkv, outb, nullptr, nullptr, 1, 16, 2, 128, 0.088f, 0.f, &z), WAN_OK);
+  EXPECT_EQ(validate_attn_skip(qkv, outb, nullptr, nullptr, 1, 16, 2, 128, 0.088f, -1e-3f, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn_skip(qkv, outb, nullptr, nullptr, 1, 16, 2, 128, 0.088f, nan, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn_skip(qkv, outb, nullptr, nullptr, 1, 16, 2, 128, 0.088f, INFINITY, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_attn_skip(qkv, outb, nullptr, buf + 100, 1, 16, 2, 128, 0.088f, 0.02f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_skip(qkv, outb, nullptr, outb + 7, 1, 16, 2, 128, 0.088f, 0.02f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_skip(qkv, outb, lseb, reinterpret_cast<unsigned char*>(lseb) + 1, 1, 16, 2, 128, 0.088f,
+                               0.02f, &z), WAN_E_ALIAS);
+  EXPECT_EQ(validate_attn_skip(nullptr, nullptr, nullptr, nullptr, 0, 16, 2, 128, 0.088f, 0.02f, &z), WAN_OK);
+  int64_t mb = 0;
+  EXPECT_EQ(skip_map_bytes(2, 100, 3, &mb), 1);
+  EXPECT_EQ(mb, 2 * 3 * 3 * 2);  // ceil(100/48) = 3 query blocks, ceil(100/64) = 2 key blocks
+  EXPECT_EQ(skip_map_bytes(INT64_MAX / 2, 1000, 256, &mb), 0);
+
   int64_t vtb = 0;
   EXPECT_EQ(fp8_vt_bytes(2, 129, 3, &vtb), 1);
   EXPECT_EQ(vtb, 2 * 3 * 128 * 256);

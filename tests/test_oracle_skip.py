@@ -147,3 +147,16 @@ def test_imposed_decisions_are_used():
     ob, _ = wan_ref.attention_ref(q, k[keys], v[keys], SCALE)
     np.testing.assert_array_equal(kept, forced)
     np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-14)
+
+
+def test_history_judges_later_blocks_after_an_imposed_decision():
+    """With a history, each block is judged by the rule given the imposed
+    earlier decisions: in the three-block case above (threshold 2), imposing
+    'kept' on block 1 raises the running max to 0.5, so block 2 (d = 0.4 <
+    ln 2) is then skipped by the rule."""
+    s = np.array([[0.0, 0.5, 0.9]])
+    kept, margin = wan_ref.skip_blocks_ref(s, 2.0, 1, 1, history=np.array([[True, True, True]]))
+    np.testing.assert_array_equal(kept, [[True, False, False]])
+    np.testing.assert_allclose(margin[0, 2], abs(0.4 - math.log(2.0)), rtol=1e-12)
+    same, _ = wan_ref.skip_blocks_ref(s, 2.0, 1, 1, history=np.array([[True, False, True]]))
+    np.testing.assert_array_equal(same, wan_ref.skip_blocks_ref(s, 2.0, 1, 1)[0])

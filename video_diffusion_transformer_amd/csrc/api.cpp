@@ -169,6 +169,25 @@ int wan_attn_fwd(const void* qkv, void* out, float* lse, int64_t B, int64_t S, i
   return WAN_OK;
 }
 
+int wan_attn_fwd_skip(const void* qkv, void* out, float* lse, uint8_t* kept, int64_t B, int64_t S, int64_t heads,
+                      int64_t head_dim, float softmax_scale, float threshold, void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_attn_skip(qkv, out, lse, kept, B, S, heads, head_dim, softmax_scale, threshold, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (B > INT32_MAX) return WAN_E_OVERFLOW;
+  if (wan::launch_attn_fwd_skip(qkv, out, lse, kept, static_cast<int>(B), static_cast<int>(S),
+                                static_cast<int>(heads), softmax_scale, threshold,
+                                static_cast<hipStream_t>(stream)) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
+int64_t wan_attn_skip_map_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim) {
+  if (B < 0 || S < 0 || heads < 0 || head_dim != wan::kHeadDim) return -1;
+  int64_t n;
+  return wan::skip_map_bytes(B, S, heads, &n) ? n : -1;
+}
+
 int wan_attn_fwd_chunk(const void* q_src, int64_t Sq, const void* kv_src, int64_t Skv, float* out, float* lse,
                        int64_t B, int64_t heads, int64_t head_dim, float softmax_scale, void* stream) {
   wan::Sizes z;

@@ -45,6 +45,8 @@
 //   * workgroups are numbered so that consecutive q-tiles of the same head land
 //     on the same XCD (blocks are dispatched round-robin over the 8 XCDs), and
 //     that XCD's L2 serves the head's K/V to all of them.
+#include <cmath>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -297,6 +299,70 @@ __device__ __forceinline__ void tile_pv(const TileArgs& a, const unsigned char* 
   }
 }
 
+// Skip-Softmax, threshold mode (the vLLM-Omni recipe "Wan2.2 Text-to-Video",
+// Skip-Softmax controls: a direct skip threshold, no calibration). The rule
+// (the pages give only the knob): keys go in tiles of 64 in increasing order;
+// a tile's softmax and PV are skipped for a wave's 48 query rows when, for
+// every one of them, exp(tile max - running max) < threshold, the running max
+// being that of the softmax, i.e. of the tiles kept so far. The scores of
+// every tile are computed (the decision needs them); a kept tile runs the
+// softmax against the exact running max (no lazy rescale: p <= 1).
+struct SkipArgs {
+  float thr_log2;  // log2(threshold) in the scaled log2 units of the scores; -inf keeps every tile
+  uint8_t* kept;   // optional decision map [B*heads][nqb][nkt] (1 = kept), or null
+  int nqb;         // query blocks (of 48 rows) per (b, h)
+};
+
+// Returns whether the wave keeps this tile; for a kept tile updates the
+// running max, row sums and output accumulator and leaves the tile's bf16 P
+// in pf.
+template <bool ExactSum>
+__device__ __forceinline__ bool skip_softmax_step(const TileArgs& a, int k0, float thr_log2, f32x4_t (&acc_s)[4][kQT],
+                                                  float (&m_run)[kQT], float (&acc_l)[kQT], f32x4_t (&acc_o)[8][kQT],
+                                                  bf16x8_t (&pf)[kQT][2]) {
+  if (k0 + kBN > a.S) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + 16 * t + 4 * a.grp + i >= a.S) {
+#pragma unroll
+          for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
+        }
+  }
+  float mx[kQT];
+  bool need = false;
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) {
+    float m = fmaxf(fmaxf(acc_s[0][u][0], acc_s[0][u][1]), fmaxf(acc_s[0][u][2], acc_s[0][u][3]));
+#pragma unroll
+    for (int t = 1; t < 4; ++t) m = fmaxf(m, fmaxf(fmaxf(acc_s[t][u][0], acc_s[t][u][1]), fmaxf(acc_s[t][u][2], acc_s[t][u][3])));
+    m *= a.scale_log2;
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));  // the column max: every lane of the query holds it
+    mx[u] = m;
+    need = need || (m - m_run[u] >= thr_log2);  // m_run = -inf before the first tile: always kept
+  }
+  if (!__ballot(need)) return false;
+#pragma unroll
+  for (int u = 0; u < kQT; ++u)
+    if (__ballot(mx[u] > m_run[u])) {
+      const float m_new = fmaxf(m_run[u], mx[u]);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);  // 0 on the first tile
+      m_run[u] = m_new;
+      acc_l[u] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_o[dt][u][i] *= alpha;
+    }
+  float lt[kQT];
+  tile_exp<ExactSum>(a, acc_s, m_run, pf, lt);
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) acc_l[u] += lt[u];
+  return true;
+}
+
 // Queries come from the Q part of one packed buffer (Sq rows per batch entry),
 // keys and values from the K and V parts of another (Skv rows); for full
 // attention both are the same buffer. The output mode: bf16 O (full
@@ -305,11 +371,11 @@ __device__ __forceinline__ void tile_pv(const TileArgs& a, const unsigned char* 
 // round with the merge in the epilogue, out16 optionally receiving a bf16 copy).
 enum OutMode { kOutBf16 = 0, kOutF32 = 1, kOutFold = 2 };
 
-template <int Mode, bool ExactSum>
+template <int Mode, bool ExactSum, bool Skip>
 __global__ void __launch_bounds__(kThreads, (kQT >= 4 || kWaves > 4) ? 1 : 2)
 attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ kvsrc, void* __restrict__ out,
                 float* __restrict__ lse, uint16_t* __restrict__ out16, int Sq, int S, int heads, int nqt,
-                float scale_log2) {
+                float scale_log2, SkipArgs sk) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStage];
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -377,6 +443,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
   }
 
   float alpha[kQT];
+  if constexpr (Skip) {
+#pragma unroll
+    for (int u = 0; u < kQT; ++u) m_run[u] = -INFINITY;  // exact running max: no tile seen yet
+  }
+  const int qblock = qt * kWaves + wave;  // Skip: this wave's 48-row query block
   f32x4_t acc_s[4][kQT];
   bf16x8_t pf[kQT][2];
   issue_tile(a, 0, smem, 0);
@@ -396,13 +467,22 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // 1 copy
     }
-    const unsigned moved = tile_softmax<ExactSum>(a, kt * kBN, acc_s, m_run, acc_l, alpha, pf);
-    if (moved) tile_rescale(moved, alpha, acc_o);
-    // Let the next tile's direct-to-LDS writes finish before the transposed V
-    // reads: measured, the PV phase runs faster without those writes competing
-    // for the LDS, and the loads have had the score and softmax phases to land.
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    tile_pv(a, smem, cur, pf, acc_o);
+    if constexpr (Skip) {
+      const bool keep = skip_softmax_step<ExactSum>(a, kt * kBN, sk.thr_log2, acc_s, m_run, acc_l, acc_o, pf);
+      if (sk.kept && lane == 0 && qblock < sk.nqb) sk.kept[((int64_t)bh * sk.nqb + qblock) * a.nkt + kt] = keep;
+      if (keep) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+        tile_pv(a, smem, cur, pf, acc_o);
+      }
+    } else {
+      const unsigned moved = tile_softmax<ExactSum>(a, kt * kBN, acc_s, m_run, acc_l, alpha, pf);
+      if (moved) tile_rescale(moved, alpha, acc_o);
+      // Let the next tile's direct-to-LDS writes finish before the transposed V
+      // reads: measured, the PV phase runs faster without those writes competing
+      // for the LDS, and the loads have had the score and softmax phases to land.
+      __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+      tile_pv(a, smem, cur, pf, acc_o);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of tile kt+1 has landed
     __syncthreads();                          // ... and every wave's; this stage is free again
   }
@@ -471,12 +551,13 @@ hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S,
   const auto* src = static_cast<const uint16_t*>(qkv);
   // The LSE-free instance (the attention step) normalises by the sum of the
   // bf16 weights; the one that also returns the LSE sums the fp32 weights.
+  const SkipArgs none{-INFINITY, nullptr, 0};
   if (lse)
-    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
-                       stream, src, src, out, lse, nullptr, S, S, heads, nqt, scale_log2);
+    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, true, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                       0, stream, src, src, out, lse, nullptr, S, S, heads, nqt, scale_log2, none);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
-                       stream, src, src, out, nullptr, nullptr, S, S, heads, nqt, scale_log2);
+    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, false, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                       0, stream, src, src, out, nullptr, nullptr, S, S, heads, nqt, scale_log2, none);
   return hipGetLastError();
 }
 
@@ -486,9 +567,9 @@ hipError_t launch_attn_fwd_chunk(const void* q_src, int Sq, const void* kv_src, 
   const int64_t nblocks = (int64_t)nqt * heads * B;
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_fwd_kernel<kOutF32, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), out, lse, nullptr, Sq,
-                     Skv, heads, nqt, scale_log2);
+  hipLaunchKernelGGL((attn_fwd_kernel<kOutF32, true, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), out, lse,
+                     nullptr, Sq, Skv, heads, nqt, scale_log2, SkipArgs{-INFINITY, nullptr, 0});
   return hipGetLastError();
 }
 
@@ -499,9 +580,30 @@ hipError_t launch_attn_fwd_chunk_fold(const void* q_src, int Sq, const void* kv_
   const int64_t nblocks = (int64_t)nqt * heads * B;
   if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_fwd_kernel<kOutFold, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), acc, acc_lse,
-                     static_cast<uint16_t*>(out16), Sq, Skv, heads, nqt, scale_log2);
+  hipLaunchKernelGGL((attn_fwd_kernel<kOutFold, true, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                     0, stream, static_cast<const uint16_t*>(q_src), static_cast<const uint16_t*>(kv_src), acc, acc_lse,
+                     static_cast<uint16_t*>(out16), Sq, Skv, heads, nqt, scale_log2, SkipArgs{-INFINITY, nullptr, 0});
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_skip(const void* qkv, void* out, float* lse, uint8_t* kept, int B, int S, int heads,
+                                float softmax_scale, float threshold, hipStream_t stream) {
+  static_assert(kQT * 16 == kSkipBlockQ && kBN == kSkipBlockK, "skip blocks are a wave's rows and one key tile");
+  const int nqt = (S + kBM - 1) / kBM;
+  const int64_t nblocks = (int64_t)nqt * heads * B;
+  if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  // exp(d) < threshold <=> d * log2(e) < log2(threshold), d in natural units;
+  // the kernel's scores are already in scaled log2 units
+  const SkipArgs sk{threshold > 0.f ? static_cast<float>(std::log2(static_cast<double>(threshold))) : -INFINITY, kept,
+                    (S + kSkipBlockQ - 1) / kSkipBlockQ};
+  const auto* src = static_cast<const uint16_t*>(qkv);
+  if (lse)
+    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, true, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                       0, stream, src, src, out, lse, nullptr, S, S, heads, nqt, scale_log2, sk);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<kOutBf16, false, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                       0, stream, src, src, out, nullptr, nullptr, S, S, heads, nqt, scale_log2, sk);
   return hipGetLastError();
 }
 

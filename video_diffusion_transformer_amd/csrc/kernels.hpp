@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wan_attn.h"
+
 namespace wan {
 
 // Q/K RMSNorm + bf16 + 3-D RoPE, in place, rows [row0, row0 + rows) of the
@@ -19,6 +21,13 @@ hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const f
 // bf16 attention forward over the packed buffer.
 hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S, int heads,
                            float softmax_scale, hipStream_t stream);
+
+// Skip-Softmax (threshold mode) variant of it; kept (optional) receives the
+// per-(query block, key tile) decisions.
+constexpr int kSkipBlockQ = WAN_SKIP_BLOCK_Q;
+constexpr int kSkipBlockK = WAN_SKIP_BLOCK_K;
+hipError_t launch_attn_fwd_skip(const void* qkv, void* out, float* lse, uint8_t* kept, int B, int S, int heads,
+                                float softmax_scale, float threshold, hipStream_t stream);
 
 // Attention of the queries of q_src (Sq rows per batch entry) against the
 // keys/values of kv_src (Skv rows), fp32 output and log-sum-exp.

@@ -119,6 +119,30 @@ inline bool kv_chunk_bytes(int64_t B, int64_t Skv, int64_t D, int64_t* out) {
   return mul_ok(B, Skv, &t) && mul_ok(t, 3 * D, &t) && mul_ok(t, 2, out);
 }
 
+// Bytes of the Skip-Softmax decision map: B * heads * ceil(S/BQ) * ceil(S/BK).
+inline bool skip_map_bytes(int64_t B, int64_t S, int64_t heads, int64_t* out) {
+  if (S < 0 || S > INT64_MAX - WAN_SKIP_BLOCK_Q) return false;
+  const int64_t nqb = (S + WAN_SKIP_BLOCK_Q - 1) / WAN_SKIP_BLOCK_Q, nkb = (S + WAN_SKIP_BLOCK_K - 1) / WAN_SKIP_BLOCK_K;
+  int64_t t;
+  return mul_ok(B, heads, &t) && mul_ok(t, nqb, &t) && mul_ok(t, nkb, out);
+}
+
+// Attention with Skip-Softmax: the checks of validate_attn, a finite
+// threshold >= 0, and the optional decision map distinct from the other buffers.
+inline int validate_attn_skip(const void* qkv, const void* out, const void* lse, const void* kept, int64_t B,
+                              int64_t S, int64_t heads, int64_t head_dim, float scale, float threshold, Sizes* z) {
+  int rc = validate_attn(qkv, out, lse, B, S, heads, head_dim, scale, 2, z);
+  if (rc != WAN_OK) return rc;
+  if (!finite(threshold) || threshold < 0.f) return WAN_E_VALUE;
+  if (z->empty || !kept) return WAN_OK;
+  int64_t map_bytes;
+  if (!skip_map_bytes(B, S, heads, &map_bytes)) return WAN_E_OVERFLOW;
+  if (overlaps(kept, map_bytes, qkv, z->qkv_elems * 2) || overlaps(kept, map_bytes, out, z->out_elems * 2) ||
+      (lse && overlaps(kept, map_bytes, lse, z->lse_bytes)))
+    return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 inline int validate_attn_chunk(const void* q_src, const void* kv_src, const void* out, const void* lse, int64_t B,
                                int64_t Sq, int64_t Skv, int64_t heads, int64_t head_dim, float scale, Sizes* z) {
   if (Skv < 0) return WAN_E_SHAPE;

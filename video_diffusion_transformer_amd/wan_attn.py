@@ -6,7 +6,7 @@ live on the GPU; there is no CPU path. If the library is not built the first
 call raises -- nothing falls back to another implementation.
 
 The names follow the C ABI: ``token_grid`` -> wan_token_grid, ``qkv_proj`` -> wan_qkv_proj,
-``qknorm_rope`` -> wan_qknorm_rope, ``attn_fwd`` -> wan_attn_fwd,
+``qknorm_rope`` -> wan_qknorm_rope, ``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_skip`` -> wan_attn_fwd_skip,
 ``attn_fwd_chunk`` -> wan_attn_fwd_chunk, ``attn_merge`` -> wan_attn_merge,
 ``attn_fwd_chunk_merge`` -> wan_attn_fwd_chunk_merge,
 ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
@@ -41,6 +41,8 @@ SIGNATURES = {
     "wan_qkv_proj": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
+    "wan_attn_fwd_skip": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _F, _P]),
+    "wan_attn_skip_map_bytes": (ctypes.c_int64, [_I64, _I64, _I64, _I64]),
     "wan_attn_fwd_chunk": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _P]),
     "wan_attn_merge": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_attn_fwd_chunk_merge": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _F, _P]),
@@ -180,6 +182,47 @@ def attn_fwd(qkv, heads, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=Fa
             _ptr(qkv), _ptr(out), _ptr(lse) if want_lse else ctypes.c_void_p(0), B, S, heads,
             head_dim, scale, _stream(qkv.device, stream)))
     return (out, lse) if want_lse else out
+
+
+SKIP_BLOCK_Q, SKIP_BLOCK_K = 48, 64  # WAN_SKIP_BLOCK_Q, WAN_SKIP_BLOCK_K of the header
+
+
+def attn_fwd_skip(qkv, heads, threshold, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=False, kept=False,
+                  stream=None):
+    """Attention with Skip-Softmax in threshold mode over a packed bf16
+    [B, S, 3*D] tensor. Returns out, followed by lse [B, heads, S] and/or the
+    decision map kept [B, heads, ceil(S/48), ceil(S/64)] (uint8, 1 = kept)
+    when those are requested (True or a preallocated tensor)."""
+    _need_gpu("qkv", qkv, torch.bfloat16)
+    B, S = qkv.shape[0], qkv.shape[1]
+    D = heads * head_dim
+    if qkv.dim() != 3 or qkv.shape[2] != 3 * D:
+        raise ValueError(f"qkv must be [B, S, {3 * D}], got {tuple(qkv.shape)}")
+    scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=qkv.device)
+    want_lse = lse is not False and lse is not None
+    if lse is True:
+        lse = torch.empty((B, heads, S), dtype=torch.float32, device=qkv.device)
+    check_attn_outputs(out, lse if want_lse else None, B, S, heads, head_dim)
+    _need_gpu("out", out, torch.bfloat16)
+    if want_lse:
+        _need_gpu("lse", lse, torch.float32)
+    want_kept = kept is not False and kept is not None
+    map_shape = (B, heads, -(-S // SKIP_BLOCK_Q), -(-S // SKIP_BLOCK_K))
+    if kept is True:
+        kept = torch.empty(map_shape, dtype=torch.uint8, device=qkv.device)
+    if want_kept:
+        _need_gpu("kept", kept, torch.uint8)
+        if tuple(kept.shape) != map_shape:
+            raise ValueError(f"kept must be {map_shape}")
+    with torch.cuda.device(qkv.device):
+        _check("wan_attn_fwd_skip", lib().wan_attn_fwd_skip(
+            _ptr(qkv), _ptr(out), _ptr(lse) if want_lse else ctypes.c_void_p(0),
+            _ptr(kept) if want_kept else ctypes.c_void_p(0), B, S, heads, head_dim, scale, float(threshold),
+            _stream(qkv.device, stream)))
+    res = (out,) + ((lse,) if want_lse else ()) + ((kept,) if want_kept else ())
+    return res[0] if len(res) == 1 else res
 
 
 def attn_fwd_chunk(q_src, kv_src, heads, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=None, stream=None):
