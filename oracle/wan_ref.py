@@ -331,6 +331,40 @@ def quant_fp8_ref(qkv, heads, head_dim):
             "codes": np.concatenate(codes, axis=-1), "deq": np.concatenate(deq, axis=-1)}
 
 
+def quant_fp8_delayed_ref(qkv, gamma_q, gamma_k, grid, heads, head_dim, amax_prev,
+                          eps=RMS_EPS, theta=ROPE_THETA):
+    """The norm + RoPE step followed by the per-tensor e4m3 quantisation with
+    a DELAYED scale: the producer does not know the amax of the tensor it is
+    writing, so each tensor's scale comes from the amax the previous call
+    reported (scale = 448 / amax_prev in fp32, 1 when that amax is 0), and the
+    call reports the amax of what it quantised for the next one ([P5] change
+    2 fuses amax, E4M3 scale and quantisation into the producing kernel; with a
+    per-tensor scale a single pass can only use an earlier amax -- the reading
+    taken here). A value with |x * scale| > 448 saturates to +-448.
+
+    qkv: [B, S, 3D] fp64 (bf16 values) before the norm; amax_prev: three
+    floats (Q, K, V). Q and K are quantised as the norm + RoPE step would
+    store them (out16 of ``qknorm_rope_ref``), V as it is. Returns a dict with
+    ``scale`` [3] (the scales used), ``amax`` [3] (of the values quantised),
+    ``codes`` ([B, S, 3D] uint8) and ``deq`` (fp64 code / scale)."""
+    T, H, W = grid
+    B, S = qkv.shape[0], qkv.shape[1]
+    D = heads * head_dim
+    r = qknorm_rope_ref(qkv, gamma_q, gamma_k, grid, heads, head_dim, eps, theta)
+    parts = [r["out16_q"].reshape(B, S, D), r["out16_k"].reshape(B, S, D),
+             np.asarray(qkv, np.float64)[..., 2 * D:]]
+    scale, amax, codes, deq = [], [], [], []
+    for x, ap in zip(parts, amax_prev):
+        sc = fp8_scale(ap)
+        v8 = e4m3_rne_sat(f32(x * sc))
+        scale.append(sc)
+        amax.append(float(np.max(np.abs(x))) if x.size else 0.0)
+        codes.append(e4m3_encode(v8))
+        deq.append(v8 / sc)
+    return {"scale": np.array(scale), "amax": np.array(amax),
+            "codes": np.concatenate(codes, axis=-1), "deq": np.concatenate(deq, axis=-1)}
+
+
 def qkv_proj_ref(x, w, bias=None):
     """The QKV projection whose output is the packed [Q|K|V] buffer.
 

@@ -56,3 +56,56 @@ def test_all_zero_tensor():
     r = wan_ref.quant_fp8_ref(x, 1, 128)
     assert list(r["scale"]) == [1.0, 1.0, 1.0]
     assert np.all(r["codes"] == 0) and np.all(r["deq"] == 0)
+
+
+def _normed_buffer(rng, B, grid, heads):
+    D = heads * 128
+    S = grid[0] * grid[1] * grid[2]
+    x = bf16_rne(rng.standard_normal((B, S, 3 * D)))
+    g = bf16_rne(1 + 0.1 * rng.standard_normal((2, D)))
+    r = wan_ref.qknorm_rope_ref(x, g[0], g[1], grid, heads, 128)
+    normed = x.copy().reshape(B * S, 3 * D)
+    normed[:, :D] = r["out16_q"]
+    normed[:, D:2 * D] = r["out16_k"]
+    return x, g, normed.reshape(B, S, 3 * D)
+
+
+def test_delayed_scale_from_the_true_amax_equals_current_scaling():
+    """Given the amax of the tensors it writes (as a previous call on the same
+    data reports), the delayed producer's codes, scales and amax equal the
+    current-scale recipe on the norm step's output."""
+    rng = np.random.default_rng(3)
+    grid, heads = (2, 3, 5), 2
+    x, g, normed = _normed_buffer(rng, 2, grid, heads)
+    cur = wan_ref.quant_fp8_ref(normed, heads, 128)
+    d = wan_ref.quant_fp8_delayed_ref(x, g[0], g[1], grid, heads, 128, cur["amax"])
+    np.testing.assert_array_equal(d["codes"], cur["codes"])
+    np.testing.assert_array_equal(d["scale"], cur["scale"])
+    np.testing.assert_array_equal(d["amax"], cur["amax"])
+    np.testing.assert_array_equal(d["deq"], cur["deq"])
+
+
+def test_delayed_scale_saturates_and_follows_the_given_scale():
+    """An earlier amax 4x smaller than the data's makes the scale 4x larger:
+    every value beyond 448 / scale saturates to +-448 (codes 0x7E / 0xFE), the
+    others are the e4m3 rounding at that scale (torch's cast, a library
+    routine), and the reported amax is the data's own; amax 0 gives scale 1."""
+    rng = np.random.default_rng(4)
+    grid, heads = (1, 4, 6), 1
+    x, g, normed = _normed_buffer(rng, 1, grid, heads)
+    D = heads * 128
+    true_amax = wan_ref.quant_fp8_ref(normed, heads, 128)["amax"]
+    d = wan_ref.quant_fp8_delayed_ref(x, g[0], g[1], grid, heads, 128, true_amax / 4)
+    np.testing.assert_array_equal(d["amax"], true_amax)
+    for i in range(3):
+        part = normed[..., i * D:(i + 1) * D]
+        sc = d["scale"][i]
+        assert sc == float(np.float32(448.0) / np.float32(true_amax[i] / 4))
+        codes = d["codes"][..., i * D:(i + 1) * D]
+        big = np.abs(np.float32(part * sc).astype(np.float64)) > 464.0  # past the last rounding midpoint
+        assert big.any()
+        assert np.all(np.isin(codes[big], [0x7E, 0xFE]))
+        y = torch.from_numpy((part * sc).astype(np.float32)).clamp(-448, 448)
+        np.testing.assert_array_equal(codes, y.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    z = wan_ref.quant_fp8_delayed_ref(x, g[0], g[1], grid, heads, 128, [0.0, 0.0, 0.0])
+    assert list(z["scale"]) == [1.0, 1.0, 1.0]
