@@ -345,6 +345,46 @@ int wan_qknorm_rope_quant_fp8(void *qkv, const void *gamma_q, const void *gamma_
                               int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
                               void *qk8, void *vt8, float *scales, float *amax, void *stream);
 
+/*
+ * wan_qknorm_rope_quant_fp8_delayed -- the single-pass fp8 producer: the norm
+ * + RoPE of wan_qknorm_rope and the e4m3 quantisation of wan_qkv_quant_fp8 in
+ * one pass over Q and K and one over V, with DELAYED per-tensor scales
+ * ("Optimize Wan2.2 Dataflow", change 2: amax, E4M3 scale and quantisation in
+ * the producing kernel). One scale per tensor cannot come from the amax of
+ * the tensor being written in a single pass, so each tensor's scale is taken
+ * from the amax an earlier call reported (for the DiT: the previous layer or
+ * step), and the call reports the amax of what it wrote for the next one:
+ *   scale[X] = 448 / amax_prev[X] (fp32 IEEE division; 1 if amax_prev[X] is 0)
+ *   x8       = e4m3( fl32(x * scale[X]) ), round to nearest even; a value with
+ *              |x * scale| > 448 saturates to +-448
+ *   amax[X]  = max |x| over the tensor quantised (the bf16 Q and K the norm +
+ *              RoPE step produces -- bit-identical to wan_qknorm_rope's -- and V)
+ * With amax_prev equal to the data's own amax, every output equals
+ * wan_qknorm_rope followed by wan_qkv_quant_fp8 (the current-scale recipe).
+ *
+ *   qkv        bf16 [B, S, 3*D], S = T*H*W: READ ONLY (the bf16 result is not
+ *              written back; Q and K reach attention as e4m3 only).
+ *   gamma_q, gamma_k, B, T, H, W, heads, head_dim, eps, theta: as wan_qknorm_rope.
+ *   amax_prev  device float[3] input: earlier amax of Q, K, V.
+ *   qk8, vt8   e4m3 outputs, layouts as wan_qkv_quant_fp8.
+ *   scales     device float[3] output: the scales used (what wan_attn_fwd_fp8
+ *              takes).
+ *   amax       device float[3] output: amax of this call's Q, K, V (cleared by
+ *              the call; pass it as amax_prev to the next call, into a
+ *              different buffer).
+ * Reads 4*D + 2*D bytes and writes 3*D bytes per token (the two-call path
+ * reads and writes the bf16 Q and K in place and reads Q, K, V once more).
+ * Three kernels on `stream` (clear amax, norm + RoPE + e4m3 Q/K, e4m3 V^T).
+ * Outputs must not overlap each other, qkv, the gammas or amax_prev. Calls
+ * that share `amax` must not overlap in time.
+ * Errors: those of wan_qknorm_rope_quant_fp8; WAN_E_NULL / WAN_E_ALIGN /
+ * WAN_E_ALIAS also for amax_prev.
+ */
+int wan_qknorm_rope_quant_fp8_delayed(const void *qkv, const void *gamma_q, const void *gamma_k, int64_t B,
+                                      int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps,
+                                      float theta, const float *amax_prev, void *qk8, void *vt8, float *scales,
+                                      float *amax, void *stream);
+
 /* Bytes of the vt8 buffer for (B, S, heads, head_dim); -1 on invalid sizes or
  * overflow. Pure host arithmetic. */
 int64_t wan_fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim);

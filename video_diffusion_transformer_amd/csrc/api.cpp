@@ -157,6 +157,34 @@ int wan_qknorm_rope_quant_fp8(void* qkv, const void* gamma_q, const void* gamma_
   return WAN_OK;
 }
 
+int wan_qknorm_rope_quant_fp8_delayed(const void* qkv, const void* gamma_q, const void* gamma_k, int64_t B, int64_t T,
+                                      int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
+                                      const float* amax_prev, void* qk8, void* vt8, float* scales, float* amax,
+                                      void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_qknorm_rope_fp8_delayed(qkv, gamma_q, gamma_k, B, T, H, W, heads, head_dim, eps, theta,
+                                                 amax_prev, qk8, vt8, scales, amax, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  if (T > INT32_MAX / 22 || H > INT32_MAX / 21 || W > INT32_MAX / 21) return WAN_E_OVERFLOW;
+  const float2* tab = nullptr;
+  rc = rope_table(T, H, W, theta, &tab);
+  if (rc != WAN_OK) return rc;
+  auto st = static_cast<hipStream_t>(stream);
+  if (wan::launch_amax_clear(amax, st) != hipSuccess) return WAN_E_HIP;
+  for (int64_t r0 = 0; r0 < z.rows; r0 += kMaxRowsPerLaunch) {
+    const int64_t n = z.rows - r0 < kMaxRowsPerLaunch ? z.rows - r0 : kMaxRowsPerLaunch;
+    // the kernel reads qkv and writes qk8 only (never the packed buffer) in this mode
+    if (wan::launch_qknorm_rope(const_cast<void*>(qkv), gamma_q, gamma_k, tab, r0, n, static_cast<int>(z.S),
+                                static_cast<int>(T), static_cast<int>(H), static_cast<int>(W), static_cast<int>(z.D),
+                                eps, amax, st, static_cast<uint8_t*>(qk8), amax_prev) != hipSuccess)
+      return WAN_E_HIP;
+  }
+  if (wan::launch_quant_v_delayed(qkv, vt8, amax_prev, scales, amax, static_cast<int>(B), static_cast<int>(z.S),
+                                  static_cast<int>(heads), st) != hipSuccess)
+    return WAN_E_HIP;
+  return WAN_OK;
+}
+
 int wan_attn_fwd(const void* qkv, void* out, float* lse, int64_t B, int64_t S, int64_t heads,
                  int64_t head_dim, float softmax_scale, void* stream) {
   wan::Sizes z;

@@ -313,13 +313,11 @@ struct SkipArgs {
   int nqb;         // query blocks (of 48 rows) per (b, h)
 };
 
-// Returns whether the wave keeps this tile; for a kept tile updates the
-// running max, row sums and output accumulator and leaves the tile's bf16 P
-// in pf.
-template <bool ExactSum>
-__device__ __forceinline__ bool skip_softmax_step(const TileArgs& a, int k0, float thr_log2, f32x4_t (&acc_s)[4][kQT],
-                                                  float (&m_run)[kQT], float (&acc_l)[kQT], f32x4_t (&acc_o)[8][kQT],
-                                                  bf16x8_t (&pf)[kQT][2]) {
+// The decision for one tile: masks keys past the end, leaves the column
+// max of each query tile in mx (scaled log2 units) and returns whether some
+// query of the wave has exp(tile max - running max) >= threshold.
+__device__ __forceinline__ bool skip_decide(const TileArgs& a, int k0, float thr_log2, f32x4_t (&acc_s)[4][kQT],
+                                            const float (&m_run)[kQT], float (&mx)[kQT]) {
   if (k0 + kBN > a.S) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -330,7 +328,6 @@ __device__ __forceinline__ bool skip_softmax_step(const TileArgs& a, int k0, flo
           for (int u = 0; u < kQT; ++u) acc_s[t][u][i] = -INFINITY;
         }
   }
-  float mx[kQT];
   bool need = false;
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
@@ -343,7 +340,15 @@ __device__ __forceinline__ bool skip_softmax_step(const TileArgs& a, int k0, flo
     mx[u] = m;
     need = need || (m - m_run[u] >= thr_log2);  // m_run = -inf before the first tile: always kept
   }
-  if (!__ballot(need)) return false;
+  return __ballot(need) != 0;
+}
+
+// Softmax of a kept tile against the exact running max: rescales the row sums
+// and output accumulator of the query tiles whose max moved, leaves the bf16 P in pf.
+template <bool ExactSum>
+__device__ __forceinline__ void skip_softmax(const TileArgs& a, const f32x4_t (&acc_s)[4][kQT], const float (&mx)[kQT],
+                                             float (&m_run)[kQT], float (&acc_l)[kQT], f32x4_t (&acc_o)[8][kQT],
+                                             bf16x8_t (&pf)[kQT][2]) {
 #pragma unroll
   for (int u = 0; u < kQT; ++u)
     if (__ballot(mx[u] > m_run[u])) {
@@ -360,7 +365,6 @@ __device__ __forceinline__ bool skip_softmax_step(const TileArgs& a, int k0, flo
   tile_exp<ExactSum>(a, acc_s, m_run, pf, lt);
 #pragma unroll
   for (int u = 0; u < kQT; ++u) acc_l[u] += lt[u];
-  return true;
 }
 
 // Queries come from the Q part of one packed buffer (Sq rows per batch entry),
@@ -468,9 +472,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ qsrc, const uint16_t* __restrict__ 
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // 1 copy
     }
     if constexpr (Skip) {
-      const bool keep = skip_softmax_step<ExactSum>(a, kt * kBN, sk.thr_log2, acc_s, m_run, acc_l, acc_o, pf);
+      float mx[kQT];
+      const bool keep = skip_decide(a, kt * kBN, sk.thr_log2, acc_s, m_run, mx);
       if (sk.kept && lane == 0 && qblock < sk.nqb) sk.kept[((int64_t)bh * sk.nqb + qblock) * a.nkt + kt] = keep;
       if (keep) {
+        skip_softmax<ExactSum>(a, acc_s, mx, m_run, acc_l, acc_o, pf);
         __builtin_amdgcn_s_waitcnt(kWaitVmem0);
         tile_pv(a, smem, cur, pf, acc_o);
       }

@@ -56,6 +56,57 @@ __device__ __forceinline__ float lse_fold_value(const LseFold& f, float a, float
   return fmaf(f.wa, f.acc_empty ? 0.f : a, f.wc * c);
 }
 
+// Per-tensor e4m3 scale from an amax: 448 / amax (IEEE fp32 division), or 1
+// for an all-zero tensor.
+__device__ __forceinline__ float fp8_scale_of(float amax) { return amax > 0.f ? 448.0f / amax : 1.0f; }
+
+// Eight bf16 values (one 16-byte chunk) -> eight OCP e4m3 bytes of x * s:
+// fp32 product, clamped to +-448 (saturation), round to nearest even.
+__device__ __forceinline__ uint2 quant8_e4m3(const u32x4_t v, float s) {
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float x0 = fminf(fmaxf(bf16_lo(v[2 * h]) * s, -448.f), 448.f);
+    const float x1 = fminf(fmaxf(bf16_hi(v[2 * h]) * s, -448.f), 448.f);
+    const float x2 = fminf(fmaxf(bf16_lo(v[2 * h + 1]) * s, -448.f), 448.f);
+    const float x3 = fminf(fmaxf(bf16_hi(v[2 * h + 1]) * s, -448.f), 448.f);
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, p, true);
+    w[h] = static_cast<uint32_t>(p);
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// max |x| over eight bf16 values, folded into m.
+__device__ __forceinline__ float absmax8(float m, const u32x4_t v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[j])), fabsf(bf16_hi(v[j]))));
+  return m;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Block-wide max of non-negative per-thread values folded into *target with one
+// atomic maximum on the float bits (non-negative floats order like their bits);
+// skipped when the running value is already larger. red: LDS of >= waves floats.
+__device__ __forceinline__ void block_atomic_max(float v, float* target, float* red) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.f;
+    for (int w = 0; w < nwaves; ++w) m = fmaxf(m, red[w]);
+    unsigned* p = reinterpret_cast<unsigned*>(target);
+    const unsigned bits = __float_as_uint(m);
+    if (bits > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, bits);
+  }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -14,9 +14,13 @@ namespace wan {
 // With amax non-null the kernel also folds max |x| of the rounded Q and K it
 // writes and of V into amax[0..2] (atomic maxima on the float bits; the caller
 // clears them first).
+// With qk8 non-null (and amax_prev) the rotated Q and K are not stored in
+// place but quantised to e4m3 into qk8 [rows, 2D] at the scales 448 /
+// amax_prev[0..1], and max |x| of Q and K goes to amax[0..1].
 hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const float2* tab,
                               int64_t row0, int64_t rows, int S, int T, int H, int W, int D,
-                              float eps, float* amax, hipStream_t stream);
+                              float eps, float* amax, hipStream_t stream, uint8_t* qk8 = nullptr,
+                              const float* amax_prev = nullptr);
 
 // bf16 attention forward over the packed buffer.
 hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S, int heads,
@@ -49,6 +53,10 @@ hipError_t launch_qkv_quant_fp8(const void* qkv, void* qk8, void* vt8, float* sc
 hipError_t launch_amax_clear(float* amax, hipStream_t stream);
 hipError_t launch_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, const float* amax, int B, int S,
                             int heads, hipStream_t stream);
+// V only, at the scale 448 / amax_prev[2]: vt8, scales[0..2] (all three from
+// amax_prev), max |v| into amax[2].
+hipError_t launch_quant_v_delayed(const void* qkv, void* vt8, const float* amax_prev, float* scales, float* amax,
+                                  int B, int S, int heads, hipStream_t stream);
 
 // QKV projection out[M, N] = x[M, K] w[N, K]^T (+ bias), bf16; K a multiple of
 // 64, N a multiple of 4.

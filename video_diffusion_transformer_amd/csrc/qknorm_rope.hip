@@ -19,6 +19,8 @@
 // the amax step of the amax -> E4M3 scale -> quantise recipe ("Optimize Wan2.2
 // Dataflow", change 2) moved into the norm epilogue, so the quantisation pass
 // that follows needs no separate amax pass over Q, K and V.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,23 +38,19 @@ namespace {
 
 constexpr int kPairsT = 22, kPairsH = 21, kPairsW = 21;  // 44/42/42 channels per axis
 
-__device__ __forceinline__ float absmax8(float m, const u32x4_t v) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[j])), fabsf(bf16_hi(v[j]))));
-  return m;
-}
+// What the kernel does with the rotated bf16 Q and K: store them in place;
+// store them in place and fold max |x| of Q, K and V into amax; or quantise
+// them to e4m3 at the scales of an earlier amax (qk8, not in place) and fold
+// max |x| of Q and K into amax.
+enum NormMode { kNormInPlace = 0, kNormAmax = 1, kNormFp8Delayed = 2 };
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
-template <int CPT, bool Amax>
+template <int CPT, int Mode>
 __global__ void __launch_bounds__(1024)
 qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
                    const uint16_t* __restrict__ gk, const float2* __restrict__ tab, int64_t row0,
-                   int S, int H, int W, int D, int offH, int offW, float inv_d, float eps, float* __restrict__ amax) {
+                   int S, int H, int W, int D, int offH, int offW, float inv_d, float eps, float* __restrict__ amax,
+                   uint8_t* __restrict__ qk8, const float* __restrict__ amax_prev) {
+  constexpr bool Amax = Mode != kNormInPlace;
   const int64_t row = row0 + blockIdx.x;
   const int s = static_cast<int>(row % S);
   const int f = s / (H * W), y = (s / W) % H, x = s % W;
@@ -71,6 +69,11 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
   }
   u32x4_t qv[CPT], kv[CPT];
   float sq = 0.f, sk = 0.f, mq = 0.f, mk = 0.f, mv = 0.f;
+  float sq8 = 1.f, sk8 = 1.f;  // kNormFp8Delayed: e4m3 scales of Q and K from the earlier amax
+  if constexpr (Mode == kNormFp8Delayed) {
+    sq8 = fp8_scale_of(amax_prev[0]);
+    sk8 = fp8_scale_of(amax_prev[1]);
+  }
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + i * blockDim.x;
@@ -82,7 +85,8 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
       qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * c);
       kv[i] = *reinterpret_cast<const u32x4_t*>(krow + 8 * c);
 #endif
-      if constexpr (Amax) mv = absmax8(mv, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + D + 8 * c)));
+      if constexpr (Mode == kNormAmax)
+        mv = absmax8(mv, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(krow + D + 8 * c)));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float a = bf16_lo(qv[i][j]), b = bf16_hi(qv[i][j]);
@@ -149,13 +153,22 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
         mq = absmax8(mq, qo);
         mk = absmax8(mk, ko);
       }
+      if constexpr (Mode == kNormFp8Delayed) {
+        uint8_t* orow = qk8 + row * (2 * (int64_t)D);
+        const uint2 oq = quant8_e4m3(qo, sq8), ok = quant8_e4m3(ko, sk8);
+        __builtin_nontemporal_store(oq.x, reinterpret_cast<uint32_t*>(orow + 8 * c));
+        __builtin_nontemporal_store(oq.y, reinterpret_cast<uint32_t*>(orow + 8 * c) + 1);
+        __builtin_nontemporal_store(ok.x, reinterpret_cast<uint32_t*>(orow + D + 8 * c));
+        __builtin_nontemporal_store(ok.y, reinterpret_cast<uint32_t*>(orow + D + 8 * c) + 1);
+      } else {
 #if WAN_NORM_NT & 2
-      __builtin_nontemporal_store(qo, reinterpret_cast<u32x4_t*>(qrow + 8 * c));
-      __builtin_nontemporal_store(ko, reinterpret_cast<u32x4_t*>(krow + 8 * c));
+        __builtin_nontemporal_store(qo, reinterpret_cast<u32x4_t*>(qrow + 8 * c));
+        __builtin_nontemporal_store(ko, reinterpret_cast<u32x4_t*>(krow + 8 * c));
 #else
-      *reinterpret_cast<u32x4_t*>(qrow + 8 * c) = qo;
-      *reinterpret_cast<u32x4_t*>(krow + 8 * c) = ko;
+        *reinterpret_cast<u32x4_t*>(qrow + 8 * c) = qo;
+        *reinterpret_cast<u32x4_t*>(krow + 8 * c) = ko;
 #endif
+      }
     }
   }
   if constexpr (Amax) {
@@ -172,7 +185,8 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
       pmax[wave][2] = mv;
     }
     __syncthreads();
-    if (threadIdx.x < 3) {
+    constexpr int kTensors = Mode == kNormAmax ? 3 : 2;  // the delayed mode leaves V to the V pass
+    if (threadIdx.x < kTensors) {
       float m = 0.f;
       for (int w = 0; w < nwaves; ++w) m = fmaxf(m, pmax[w][threadIdx.x]);
       unsigned* p = reinterpret_cast<unsigned*>(amax) + threadIdx.x;
@@ -186,7 +200,7 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
 
 hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const float2* tab,
                               int64_t row0, int64_t rows, int S, int T, int H, int W, int D,
-                              float eps, float* amax, hipStream_t stream) {
+                              float eps, float* amax, hipStream_t stream, uint8_t* qk8, const float* amax_prev) {
   const int nchunks = D / 8;
   int cpt = nchunks <= 1024 ? 1 : (nchunks <= 2048 ? 2 : 4);
   cpt = cpt < WAN_NORM_MIN_CPT ? WAN_NORM_MIN_CPT : cpt;
@@ -200,17 +214,17 @@ hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const f
   dim3 grid(static_cast<unsigned>(rows));
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, q, a, b, tab, row0, S, H, W, D, offH, offW, inv_d, eps,
-                       amax);
+                       amax, qk8, amax_prev);
   };
-  if (amax) {
-    if (cpt == 1) go(qknorm_rope_kernel<1, true>);
-    else if (cpt == 2) go(qknorm_rope_kernel<2, true>);
-    else go(qknorm_rope_kernel<4, true>);
-  } else {
-    if (cpt == 1) go(qknorm_rope_kernel<1, false>);
-    else if (cpt == 2) go(qknorm_rope_kernel<2, false>);
-    else go(qknorm_rope_kernel<4, false>);
-  }
+  auto pick = [&](auto mode) {
+    constexpr int M = decltype(mode)::value;
+    if (cpt == 1) go(qknorm_rope_kernel<1, M>);
+    else if (cpt == 2) go(qknorm_rope_kernel<2, M>);
+    else go(qknorm_rope_kernel<4, M>);
+  };
+  if (qk8) pick(std::integral_constant<int, kNormFp8Delayed>{});
+  else if (amax) pick(std::integral_constant<int, kNormAmax>{});
+  else pick(std::integral_constant<int, kNormInPlace>{});
   return hipGetLastError();
 }
 

@@ -67,38 +67,26 @@ __global__ void __launch_bounds__(256) amax_kernel(const uint16_t* __restrict__ 
   }
 }
 
-__device__ __forceinline__ float scale_of(float amax) { return amax > 0.f ? 448.0f / amax : 1.0f; }
-
-// Eight bf16 (one 16-byte chunk) -> eight e4m3 bytes.
-__device__ __forceinline__ uint2 quant8(const u32x4_t v, float s) {
-  uint32_t w[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float x0 = fminf(fmaxf(bf16_lo(v[2 * h]) * s, -448.f), 448.f);
-    const float x1 = fminf(fmaxf(bf16_hi(v[2 * h]) * s, -448.f), 448.f);
-    const float x2 = fminf(fmaxf(bf16_lo(v[2 * h + 1]) * s, -448.f), 448.f);
-    const float x3 = fminf(fmaxf(bf16_hi(v[2 * h + 1]) * s, -448.f), 448.f);
-    int p = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-    p = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, p, true);
-    w[h] = static_cast<uint32_t>(p);
-  }
-  return make_uint2(w[0], w[1]);
-}
-
 // One block = kTok tokens of one (b, head): Q and K rows are quantised in place
 // of their packed position; V goes through LDS to be stored channel-major.
+// VOnly (the delayed-scale producer, whose norm pass already wrote the e4m3 Q
+// and K): only V is read and quantised, with the scale of amax[2] (the amax an
+// earlier call reported), and its max |v| is folded into amax_out[2].
+template <bool VOnly>
 __global__ void __launch_bounds__(256)
 quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_t* __restrict__ vt8,
-             const float* __restrict__ amax, float* __restrict__ scales, int S, int S_pad, int heads) {
+             const float* __restrict__ amax, float* __restrict__ scales, float* __restrict__ amax_out, int S,
+             int S_pad, int heads) {
   __shared__ uint8_t vt[128][kTok + 16];
   const int h = blockIdx.y, b = blockIdx.z, s0 = blockIdx.x * kTok;
   const int D = heads * 128;
-  const float sq = scale_of(amax[0]), sk = scale_of(amax[1]), sv = scale_of(amax[2]);
+  const float sq = fp8_scale_of(amax[0]), sk = fp8_scale_of(amax[1]), sv = fp8_scale_of(amax[2]);
   if (blockIdx.x == 0 && h == 0 && b == 0 && threadIdx.x == 0) {
     scales[0] = sq;
     scales[1] = sk;
     scales[2] = sv;
   }
+  float mv = 0.f;
   // kTok tokens x 16 chunks of 8 channels, kTok / 16 per thread.
 #pragma unroll
   for (int i = 0; i < kTok / 16; ++i) {
@@ -108,27 +96,35 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
     uint2 vq = make_uint2(0, 0);
     if (s < S) {
       const uint16_t* row = qkv + ((int64_t)b * S + s) * 3 * (int64_t)D + h * 128 + 8 * ch;
-      uint8_t* orow = qk8 + ((int64_t)b * S + s) * 2 * (int64_t)D + h * 128 + 8 * ch;
+      u32x4_t xq, xk;
 #if WAN_QUANT_NT & 1
-      const u32x4_t xq = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row));
-      const u32x4_t xk = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + D));
+      if constexpr (!VOnly) {
+        xq = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row));
+        xk = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + D));
+      }
       const u32x4_t xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 2 * D));
 #else
-      const u32x4_t xq = *reinterpret_cast<const u32x4_t*>(row);
-      const u32x4_t xk = *reinterpret_cast<const u32x4_t*>(row + D);
+      if constexpr (!VOnly) {
+        xq = *reinterpret_cast<const u32x4_t*>(row);
+        xk = *reinterpret_cast<const u32x4_t*>(row + D);
+      }
       const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(row + 2 * D);
 #endif
+      if constexpr (!VOnly) {
+        uint8_t* orow = qk8 + ((int64_t)b * S + s) * 2 * (int64_t)D + h * 128 + 8 * ch;
 #if WAN_QUANT_NT & 2
-      const uint2 oq = quant8(xq, sq), ok = quant8(xk, sk);
-      __builtin_nontemporal_store(oq.x, reinterpret_cast<uint32_t*>(orow));
-      __builtin_nontemporal_store(oq.y, reinterpret_cast<uint32_t*>(orow) + 1);
-      __builtin_nontemporal_store(ok.x, reinterpret_cast<uint32_t*>(orow + D));
-      __builtin_nontemporal_store(ok.y, reinterpret_cast<uint32_t*>(orow + D) + 1);
+        const uint2 oq = quant8_e4m3(xq, sq), ok = quant8_e4m3(xk, sk);
+        __builtin_nontemporal_store(oq.x, reinterpret_cast<uint32_t*>(orow));
+        __builtin_nontemporal_store(oq.y, reinterpret_cast<uint32_t*>(orow) + 1);
+        __builtin_nontemporal_store(ok.x, reinterpret_cast<uint32_t*>(orow + D));
+        __builtin_nontemporal_store(ok.y, reinterpret_cast<uint32_t*>(orow + D) + 1);
 #else
-      *reinterpret_cast<uint2*>(orow) = quant8(xq, sq);
-      *reinterpret_cast<uint2*>(orow + D) = quant8(xk, sk);
+        *reinterpret_cast<uint2*>(orow) = quant8_e4m3(xq, sq);
+        *reinterpret_cast<uint2*>(orow + D) = quant8_e4m3(xk, sk);
 #endif
-      vq = quant8(xv, sv);
+      }
+      if constexpr (VOnly) mv = absmax8(mv, xv);
+      vq = quant8_e4m3(xv, sv);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -152,6 +148,10 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
         *reinterpret_cast<const u32x4_t*>(&vt[d][16 * part]);
 #endif
   }
+  if constexpr (VOnly) {
+    __shared__ float red[4];
+    block_atomic_max(mv, amax_out + 2, red);
+  }
 }
 
 }  // namespace
@@ -164,9 +164,18 @@ hipError_t launch_amax_clear(float* amax, hipStream_t stream) {
 hipError_t launch_quant_fp8(const void* qkv, void* qk8, void* vt8, float* scales, const float* amax, int B, int S,
                             int heads, hipStream_t stream) {
   const int S_pad = (S + 127) / 128 * 128;
-  hipLaunchKernelGGL(quant_kernel, dim3(S_pad / kTok, heads, B), dim3(256), 0, stream,
+  hipLaunchKernelGGL(quant_kernel<false>, dim3(S_pad / kTok, heads, B), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qkv), static_cast<uint8_t*>(qk8), static_cast<uint8_t*>(vt8),
-                     amax, scales, S, S_pad, heads);
+                     amax, scales, nullptr, S, S_pad, heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v_delayed(const void* qkv, void* vt8, const float* amax_prev, float* scales, float* amax,
+                                  int B, int S, int heads, hipStream_t stream) {
+  const int S_pad = (S + 127) / 128 * 128;
+  hipLaunchKernelGGL(quant_kernel<true>, dim3(S_pad / kTok, heads, B), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qkv), nullptr, static_cast<uint8_t*>(vt8), amax_prev, scales, amax,
+                     S, S_pad, heads);
   return hipGetLastError();
 }
 

@@ -266,6 +266,26 @@ inline int validate_qknorm_rope_fp8(const void* qkv, const void* gq, const void*
   return WAN_OK;
 }
 
+// Norm + RoPE + e4m3 at a delayed scale: the norm checks (qkv is only read),
+// the quantisation outputs distinct from qkv, the gammas and each other, and
+// amax_prev (read while amax is cleared and written) distinct from every output.
+inline int validate_qknorm_rope_fp8_delayed(const void* qkv, const void* gq, const void* gk, int64_t B, int64_t T,
+                                            int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps,
+                                            float theta, const void* amax_prev, const void* qk8, const void* vt8,
+                                            const void* scales, const void* amax, Sizes* z) {
+  int rc = validate_qknorm_rope_fp8(qkv, gq, gk, B, T, H, W, heads, head_dim, eps, theta, qk8, vt8, scales, amax, z);
+  if (rc != WAN_OK || z->empty) return rc;
+  if (!amax_prev) return WAN_E_NULL;
+  if (!aligned(amax_prev, 4)) return WAN_E_ALIGN;
+  int64_t vt_bytes;
+  if (!fp8_vt_bytes(B, z->S, heads, &vt_bytes)) return WAN_E_OVERFLOW;
+  const void* outs[4] = {qk8, vt8, scales, amax};
+  const int64_t sizes[4] = {z->rows * 2 * z->D, vt_bytes, 12, 12};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(outs[i], sizes[i], amax_prev, 12)) return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 inline int validate_attn_fp8(const void* qk8, const void* vt8, const void* scales, const void* out,
                              const void* lse, int64_t B, int64_t S, int64_t heads, int64_t head_dim, float scale,
                              Sizes* z) {

@@ -10,7 +10,8 @@ The names follow the C ABI: ``token_grid`` -> wan_token_grid, ``qkv_proj`` -> wa
 ``attn_fwd_chunk`` -> wan_attn_fwd_chunk, ``attn_merge`` -> wan_attn_merge,
 ``attn_fwd_chunk_merge`` -> wan_attn_fwd_chunk_merge,
 ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
-``qknorm_rope_quant_fp8`` -> wan_qknorm_rope_quant_fp8, ``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
+``qknorm_rope_quant_fp8`` -> wan_qknorm_rope_quant_fp8,
+``qknorm_rope_quant_fp8_delayed`` -> wan_qknorm_rope_quant_fp8_delayed, ``attn_fwd_fp8`` -> wan_attn_fwd_fp8.
 """
 
 import ctypes
@@ -49,6 +50,8 @@ SIGNATURES = {
     "wan_qkv_quant_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qknorm_rope_quant_fp8": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F,
                                                  _P, _P, _P, _P, _P]),
+    "wan_qknorm_rope_quant_fp8_delayed": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F,
+                                                         _P, _P, _P, _P, _P, _P]),
     "wan_fp8_vt_bytes": (ctypes.c_int64, [_I64, _I64, _I64, _I64]),
     "wan_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
 }
@@ -405,6 +408,38 @@ def qknorm_rope_quant_fp8(qkv, gamma_q, gamma_k, grid, heads, head_dim=HEAD_DIM,
     with torch.cuda.device(qkv.device):
         _check("wan_qknorm_rope_quant_fp8", lib().wan_qknorm_rope_quant_fp8(
             _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), B, T, H, W, heads, head_dim, eps, theta,
+            _ptr(f.qk8), _ptr(f.vt8), _ptr(f.scales), _ptr(f.amax), _stream(qkv.device, stream)))
+    return f
+
+
+def qknorm_rope_quant_fp8_delayed(qkv, gamma_q, gamma_k, grid, heads, amax_prev, head_dim=HEAD_DIM, eps=RMS_EPS,
+                                  theta=ROPE_THETA, out=None, stream=None):
+    """Single-pass fp8 producer with delayed scales: norm + RoPE of qkv (read
+    only) quantised to e4m3 at the scales 448 / amax_prev (a device fp32 [3]
+    tensor, e.g. the ``amax`` of an earlier call's Fp8QKV). Returns an Fp8QKV
+    whose ``scales`` are the scales used and ``amax`` this call's amax
+    (allocated unless ``out`` is given; its amax must not be amax_prev)."""
+    T, H, W = grid
+    for name, t in (("qkv", qkv), ("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        _need_gpu(name, t, torch.bfloat16)
+    _need_gpu("amax_prev", amax_prev, torch.float32)
+    B, D = qkv.shape[0], heads * head_dim
+    S = T * H * W
+    if qkv.dim() != 3 or qkv.shape[1] != S or qkv.shape[2] != 3 * D:
+        raise ValueError(f"qkv must be [B, {S}, {3 * D}], got {tuple(qkv.shape)}")
+    if gamma_q.numel() != D or gamma_k.numel() != D:
+        raise ValueError("gammas must have heads*head_dim elements")
+    if amax_prev.numel() != 3:
+        raise ValueError("amax_prev must hold 3 floats")
+    f = out if out is not None else fp8_buffers(B, S, heads, qkv.device, head_dim)
+    check_fp8_buffers(f, B, S, heads, head_dim)
+    for name in ("qk8", "vt8"):
+        _need_gpu(name, getattr(f, name), torch.uint8)
+    _need_gpu("scales", f.scales, torch.float32)
+    _need_gpu("amax", f.amax, torch.float32)
+    with torch.cuda.device(qkv.device):
+        _check("wan_qknorm_rope_quant_fp8_delayed", lib().wan_qknorm_rope_quant_fp8_delayed(
+            _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), B, T, H, W, heads, head_dim, eps, theta, _ptr(amax_prev),
             _ptr(f.qk8), _ptr(f.vt8), _ptr(f.scales), _ptr(f.amax), _stream(qkv.device, stream)))
     return f
 
