@@ -1,12 +1,10 @@
 // extern "C" entry points of libwan_attn.so: validate -> (tables) -> launch.
 #include <hip/hip_runtime.h>
 
-#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <tuple>
-#include <vector>
 
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -17,14 +15,16 @@ namespace {
 // ---------------------------------------------------------------- RoPE tables
 // fp32 (cos, sin) of pos * theta^(-2j/d_a) for the frame axis (d_a = 44, 22
 // pairs), the row axis (42, 21 pairs) and the column axis (42, 21 pairs) --
-// Wan2.2's 3-D rotary split of a 128-channel head -- computed in double on the
-// host and rounded once to fp32. One device allocation per (device, T, H, W,
-// theta), kept until the process ends.
+// Wan2.2's 3-D rotary split of a 128-channel head -- computed in double and
+// rounded once to fp32 by a device kernel (the one the allocation-free entry
+// point also uses). One device allocation per (device, T, H, W, theta), kept
+// until the process ends; built on the caller's stream, which is synchronised
+// once so that calls on other streams find it complete.
 using TabKey = std::tuple<int, int64_t, int64_t, int64_t, uint32_t>;
 std::mutex g_tab_mu;
 std::map<TabKey, float2*> g_tabs;
 
-int rope_table(int64_t T, int64_t H, int64_t W, float theta, const float2** out) {
+int rope_table(int64_t T, int64_t H, int64_t W, float theta, hipStream_t stream, const float2** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return WAN_E_HIP;
   uint32_t tbits;
@@ -36,22 +36,12 @@ int rope_table(int64_t T, int64_t H, int64_t W, float theta, const float2** out)
     *out = it->second;
     return WAN_OK;
   }
-  const int npairs[3] = {22, 21, 21};
-  const int64_t len[3] = {T, H, W};
-  std::vector<float2> host;
-  host.reserve(static_cast<size_t>(T * 22 + H * 21 + W * 21));
-  for (int a = 0; a < 3; ++a) {
-    const double da = 2.0 * npairs[a];
-    for (int64_t pos = 0; pos < len[a]; ++pos)
-      for (int j = 0; j < npairs[a]; ++j) {
-        const double omega = std::pow(static_cast<double>(theta), -2.0 * j / da);
-        const double phi = static_cast<double>(pos) * omega;
-        host.push_back(make_float2(static_cast<float>(std::cos(phi)), static_cast<float>(std::sin(phi))));
-      }
-  }
+  const int64_t n = wan::rope_table_entries(T, H, W);
   float2* dptr = nullptr;
-  if (hipMalloc(&dptr, host.size() * sizeof(float2)) != hipSuccess) return WAN_E_NOMEM;
-  if (hipMemcpy(dptr, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+  if (hipMalloc(&dptr, (n > 0 ? n : 1) * sizeof(float2)) != hipSuccess) return WAN_E_NOMEM;
+  if (wan::launch_rope_table(dptr, static_cast<int>(T), static_cast<int>(H), static_cast<int>(W), theta, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipFree(dptr);
     return WAN_E_HIP;
   }
@@ -118,7 +108,7 @@ int wan_qknorm_rope(void* qkv, const void* gamma_q, const void* gamma_k, int64_t
   if (rc != WAN_OK || z.empty) return rc;
   if (T > INT32_MAX / 22 || H > INT32_MAX / 21 || W > INT32_MAX / 21) return WAN_E_OVERFLOW;
   const float2* tab = nullptr;
-  rc = rope_table(T, H, W, theta, &tab);
+  rc = rope_table(T, H, W, theta, static_cast<hipStream_t>(stream), &tab);
   if (rc != WAN_OK) return rc;
   auto st = static_cast<hipStream_t>(stream);
   for (int64_t r0 = 0; r0 < z.rows; r0 += kMaxRowsPerLaunch) {
@@ -140,7 +130,7 @@ int wan_qknorm_rope_quant_fp8(void* qkv, const void* gamma_q, const void* gamma_
   if (rc != WAN_OK || z.empty) return rc;
   if (T > INT32_MAX / 22 || H > INT32_MAX / 21 || W > INT32_MAX / 21) return WAN_E_OVERFLOW;
   const float2* tab = nullptr;
-  rc = rope_table(T, H, W, theta, &tab);
+  rc = rope_table(T, H, W, theta, static_cast<hipStream_t>(stream), &tab);
   if (rc != WAN_OK) return rc;
   auto st = static_cast<hipStream_t>(stream);
   if (wan::launch_amax_clear(amax, st) != hipSuccess) return WAN_E_HIP;
@@ -167,7 +157,7 @@ int wan_qknorm_rope_quant_fp8_delayed(const void* qkv, const void* gamma_q, cons
   if (rc != WAN_OK || z.empty) return rc;
   if (T > INT32_MAX / 22 || H > INT32_MAX / 21 || W > INT32_MAX / 21) return WAN_E_OVERFLOW;
   const float2* tab = nullptr;
-  rc = rope_table(T, H, W, theta, &tab);
+  rc = rope_table(T, H, W, theta, static_cast<hipStream_t>(stream), &tab);
   if (rc != WAN_OK) return rc;
   auto st = static_cast<hipStream_t>(stream);
   if (wan::launch_amax_clear(amax, st) != hipSuccess) return WAN_E_HIP;

@@ -22,6 +22,11 @@ hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const f
                               float eps, float* amax, hipStream_t stream, uint8_t* qk8 = nullptr,
                               const float* amax_prev = nullptr);
 
+// The rotary tables `tab` the norm kernel reads, built on the device (fp32
+// roundings of double cos/sin) on `stream`; rope_table_entries() float2 entries.
+int64_t rope_table_entries(int64_t T, int64_t H, int64_t W);
+hipError_t launch_rope_table(float2* tab, int T, int H, int W, float theta, hipStream_t stream);
+
 // bf16 attention forward over the packed buffer.
 hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S, int heads,
                            float softmax_scale, hipStream_t stream);

@@ -196,7 +196,40 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
   }
 }
 
+// The fp32 (cos, sin) tables of the three rotary axes: entry (pos, j) of an
+// axis with np pairs holds cos / sin of pos * theta^(-2j / (2 np)), computed in
+// double and rounded once to fp32. Layout: frame axis [T][22], row axis
+// [H][21], column axis [W][21], one after the other.
+__global__ void __launch_bounds__(256) rope_table_kernel(float2* __restrict__ tab, int T, int H, int W, double theta) {
+  const int n = T * kPairsT + H * kPairsH + W * kPairsW;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  int pos, j, np;
+  if (e < T * kPairsT) {
+    pos = e / kPairsT, j = e % kPairsT, np = kPairsT;
+  } else if (e < T * kPairsT + H * kPairsH) {
+    const int r = e - T * kPairsT;
+    pos = r / kPairsH, j = r % kPairsH, np = kPairsH;
+  } else {
+    const int r = e - T * kPairsT - H * kPairsH;
+    pos = r / kPairsW, j = r % kPairsW, np = kPairsW;
+  }
+  const double omega = pow(theta, -2.0 * j / (2.0 * np));
+  const double phi = static_cast<double>(pos) * omega;
+  tab[e] = make_float2(static_cast<float>(cos(phi)), static_cast<float>(sin(phi)));
+}
+
 }  // namespace
+
+int64_t rope_table_entries(int64_t T, int64_t H, int64_t W) { return T * kPairsT + H * kPairsH + W * kPairsW; }
+
+hipError_t launch_rope_table(float2* tab, int T, int H, int W, float theta, hipStream_t stream) {
+  const int64_t n = rope_table_entries(T, H, W);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, tab, T, H,
+                     W, static_cast<double>(theta));
+  return hipGetLastError();
+}
 
 hipError_t launch_qknorm_rope(void* qkv, const void* gq, const void* gk, const float2* tab,
                               int64_t row0, int64_t rows, int S, int T, int H, int W, int D,
