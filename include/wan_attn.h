@@ -76,7 +76,8 @@ typedef enum {
   WAN_E_OVERFLOW = -6,    /* a size product overflows int64, or S exceeds 2^31-1 */
   WAN_E_HIP = -7,         /* a HIP runtime call or kernel launch failed */
   WAN_E_NOMEM = -8,       /* a library-owned table could not be allocated */
-  WAN_E_VALUE = -9        /* a scalar argument is out of range (eps, theta, scale) */
+  WAN_E_VALUE = -9,       /* a scalar argument is out of range (eps, theta, scale) */
+  WAN_E_LIMIT = -10       /* beyond the fixed capacity of an allocation-free entry point */
 } wan_status;
 
 /* Version of this ABI (WAN_ABI_VERSION of the built library). */
@@ -344,6 +345,23 @@ int wan_qkv_quant_fp8(const void *qkv, void *qk8, void *vt8, float *scales, floa
 int wan_qknorm_rope_quant_fp8(void *qkv, const void *gamma_q, const void *gamma_k, int64_t B, int64_t T,
                               int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
                               void *qk8, void *vt8, float *scales, float *amax, void *stream);
+
+/*
+ * wan_qknorm_rope_noalloc -- wan_qknorm_rope for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, same output bit for bit. It never
+ * allocates or frees: the rotary tables live in a fixed library-owned device
+ * array of 65,536 (cos, sin) entries per device (512 KiB, held until the
+ * process ends) and are rebuilt on `stream` by every call, so the grid must
+ * satisfy T*22 + H*21 + W*21 <= 65,536 (else WAN_E_LIMIT, nothing launched).
+ * Every call on a device shares that device's array: calls on one device that
+ * overlap in time (different streams, or threads without ordering) race on it.
+ * Errors: those of wan_qknorm_rope except WAN_E_NOMEM; WAN_E_LIMIT.
+ */
+int wan_qknorm_rope_noalloc(void *qkv, const void *gamma_q, const void *gamma_k,
+                            int64_t B, int64_t T, int64_t H, int64_t W,
+                            int64_t heads, int64_t head_dim,
+                            float eps, float theta, void *stream);
 
 /*
  * wan_qknorm_rope_quant_fp8_delayed -- the single-pass fp8 producer: the norm

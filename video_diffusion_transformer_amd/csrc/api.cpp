@@ -70,6 +70,7 @@ const char* wan_status_str(int status) {
     case WAN_E_HIP: return "HIP runtime error or kernel launch failure";
     case WAN_E_NOMEM: return "device allocation of a library table failed";
     case WAN_E_VALUE: return "a scalar argument is out of range";
+    case WAN_E_LIMIT: return "beyond the fixed capacity of the allocation-free entry point (rotary table entries)";
     default: return "unknown status";
   }
 }

@@ -30,6 +30,7 @@ ROPE_THETA = 10000.0
 _STATUS = {
     0: "WAN_OK", -1: "WAN_E_NULL", -2: "WAN_E_SHAPE", -3: "WAN_E_UNSUPPORTED", -4: "WAN_E_ALIGN",
     -5: "WAN_E_ALIAS", -6: "WAN_E_OVERFLOW", -7: "WAN_E_HIP", -8: "WAN_E_NOMEM", -9: "WAN_E_VALUE",
+    -10: "WAN_E_LIMIT",
 }
 
 # (name, restype, argtypes) of every symbol the header declares.
@@ -41,6 +42,7 @@ SIGNATURES = {
                                       ctypes.POINTER(_I64)]),
     "wan_qkv_proj": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
+    "wan_qknorm_rope_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
     "wan_attn_fwd_skip": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_skip_map_bytes": (ctypes.c_int64, [_I64, _I64, _I64, _I64]),
