@@ -184,6 +184,15 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
       acc_s[t][0] = mfma_fp8(a, qf[0], f32x4_t{});
       acc_s[t][1] = mfma_fp8(a, qf[1], f32x4_t{});
     }
+    // Fragment reads issued two tiles ahead of their MFMAs (R0 R1 | M0 R2 | M1
+    // R3 | ... | M7): grouped two reads then two MFMAs by the compiler, each
+    // wait for a tile's reads also waited for the next tile's (+2%).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      if (t + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
 
     if (k0 + kBN > S) {  // keys past the end (last unit only): lane group grp holds keys 32grp + 4t + i
 #pragma unroll
@@ -247,6 +256,13 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ qk8, const uint8_t* __restrict__
       const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       acc_o[dt][0] = mfma_fp8(a, pf[0], acc_o[dt][0]);
       acc_o[dt][1] = mfma_fp8(a, pf[1], acc_o[dt][1]);
+    }
+    // The same two-ahead order for the V^T fragments.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+      if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
     }
 
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's part of the next unit has landed
