@@ -12,6 +12,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
@@ -62,7 +63,7 @@ __device__ __forceinline__ float fp8_scale_of(float amax) { return amax > 0.f ? 
 
 // Eight bf16 values (one 16-byte chunk) -> eight OCP e4m3 bytes of x * s:
 // fp32 product, clamped to +-448 (saturation), round to nearest even.
-__device__ __forceinline__ uint2 quant8_e4m3(const u32x4_t v, float s) {
+__device__ __forceinline__ u32x2_t quant8_e4m3(const u32x4_t v, float s) {
   uint32_t w[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -74,7 +75,7 @@ __device__ __forceinline__ uint2 quant8_e4m3(const u32x4_t v, float s) {
     p = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, p, true);
     w[h] = static_cast<uint32_t>(p);
   }
-  return make_uint2(w[0], w[1]);
+  return u32x2_t{w[0], w[1]};
 }
 
 // max |x| over eight bf16 values, folded into m.

@@ -155,11 +155,8 @@ qknorm_rope_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ gq,
       }
       if constexpr (Mode == kNormFp8Delayed) {
         uint8_t* orow = qk8 + row * (2 * (int64_t)D);
-        const uint2 oq = quant8_e4m3(qo, sq8), ok = quant8_e4m3(ko, sk8);
-        __builtin_nontemporal_store(oq.x, reinterpret_cast<uint32_t*>(orow + 8 * c));
-        __builtin_nontemporal_store(oq.y, reinterpret_cast<uint32_t*>(orow + 8 * c) + 1);
-        __builtin_nontemporal_store(ok.x, reinterpret_cast<uint32_t*>(orow + D + 8 * c));
-        __builtin_nontemporal_store(ok.y, reinterpret_cast<uint32_t*>(orow + D + 8 * c) + 1);
+        __builtin_nontemporal_store(quant8_e4m3(qo, sq8), reinterpret_cast<u32x2_t*>(orow + 8 * c));
+        __builtin_nontemporal_store(quant8_e4m3(ko, sk8), reinterpret_cast<u32x2_t*>(orow + D + 8 * c));
       } else {
 #if WAN_NORM_NT & 2
         __builtin_nontemporal_store(qo, reinterpret_cast<u32x4_t*>(qrow + 8 * c));

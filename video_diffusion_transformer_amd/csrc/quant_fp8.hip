@@ -81,7 +81,7 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
   const int h = blockIdx.y, b = blockIdx.z, s0 = blockIdx.x * kTok;
   const int D = heads * 128;
   const float sq = fp8_scale_of(amax[0]), sk = fp8_scale_of(amax[1]), sv = fp8_scale_of(amax[2]);
-  if (blockIdx.x == 0 && h == 0 && b == 0 && threadIdx.x == 0) {
+  if (s0 == 0 && h == 0 && b == 0 && threadIdx.x == 0) {
     scales[0] = sq;
     scales[1] = sk;
     scales[2] = sv;
@@ -93,7 +93,7 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
     const int c = threadIdx.x + 256 * i;
     const int t = c >> 4, ch = c & 15;
     const int s = s0 + t;
-    uint2 vq = make_uint2(0, 0);
+    u32x2_t vq = {0u, 0u};
     if (s < S) {
       const uint16_t* row = qkv + ((int64_t)b * S + s) * 3 * (int64_t)D + h * 128 + 8 * ch;
       u32x4_t xq, xk;
@@ -113,14 +113,11 @@ quant_kernel(const uint16_t* __restrict__ qkv, uint8_t* __restrict__ qk8, uint8_
       if constexpr (!VOnly) {
         uint8_t* orow = qk8 + ((int64_t)b * S + s) * 2 * (int64_t)D + h * 128 + 8 * ch;
 #if WAN_QUANT_NT & 2
-        const uint2 oq = quant8_e4m3(xq, sq), ok = quant8_e4m3(xk, sk);
-        __builtin_nontemporal_store(oq.x, reinterpret_cast<uint32_t*>(orow));
-        __builtin_nontemporal_store(oq.y, reinterpret_cast<uint32_t*>(orow) + 1);
-        __builtin_nontemporal_store(ok.x, reinterpret_cast<uint32_t*>(orow + D));
-        __builtin_nontemporal_store(ok.y, reinterpret_cast<uint32_t*>(orow + D) + 1);
+        __builtin_nontemporal_store(quant8_e4m3(xq, sq), reinterpret_cast<u32x2_t*>(orow));
+        __builtin_nontemporal_store(quant8_e4m3(xk, sk), reinterpret_cast<u32x2_t*>(orow + D));
 #else
-        *reinterpret_cast<uint2*>(orow) = quant8_e4m3(xq, sq);
-        *reinterpret_cast<uint2*>(orow + D) = quant8_e4m3(xk, sk);
+        *reinterpret_cast<u32x2_t*>(orow) = quant8_e4m3(xq, sq);
+        *reinterpret_cast<u32x2_t*>(orow + D) = quant8_e4m3(xk, sk);
 #endif
       }
       if constexpr (VOnly) mv = absmax8(mv, xv);
