@@ -111,9 +111,8 @@ int wan_token_grid(int64_t width, int64_t height, int64_t num_frames, int64_t *T
  * fused QKV projection produces Q, K and V in one shared allocation (the
  * buffer wan_qknorm_rope and wan_attn_fwd then read in place); "Optimizing
  * High-Quality Offline Video Generation", NKI kernels: qkv_cte is this
- * projection (fused there with the norm and RoPE; a norm over the full width
- * cannot finish inside one output tile of a GEMM, so here the norm stays its
- * own pass).
+ * projection, fused there with the norm and RoPE -- wan_qkv_proj_norm_rope
+ * below is that fused form; this one leaves the norm to wan_qknorm_rope).
  *
  *   x      bf16 [B, S, D] token activations, D = heads * head_dim.
  *   w_qkv  bf16 [3*D, D]: one row per output feature (features 0..D-1 are Q,
@@ -154,10 +153,11 @@ int wan_qkv_proj(const void *x, const void *w_qkv, const void *bias, void *qkv, 
  *   eps      RMSNorm epsilon (1e-6), finite and >= 0.
  *   theta    RoPE base (10000), finite and > 0.
  *
- * The cos/sin tables of a (device, T, H, W, theta) are built once on the host
- * in double precision, rounded to fp32, and kept in a library-owned device
- * allocation for the life of the process (its first call per shape therefore
- * allocates and copies synchronously; later calls only launch).
+ * The cos/sin tables of a (device, T, H, W, theta) are computed once by a
+ * device kernel in double precision, rounded to fp32, and kept in a
+ * library-owned device allocation for the life of the process (its first call
+ * per shape therefore allocates and synchronises the stream once; later calls
+ * only launch).
  * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN (qkv, gammas
  * 16-byte), WAN_E_ALIAS (a gamma inside qkv), WAN_E_OVERFLOW, WAN_E_VALUE,
  * WAN_E_NOMEM, WAN_E_HIP.
@@ -166,6 +166,51 @@ int wan_qknorm_rope(void *qkv, const void *gamma_q, const void *gamma_k,
                     int64_t B, int64_t T, int64_t H, int64_t W,
                     int64_t heads, int64_t head_dim,
                     float eps, float theta, void *stream);
+
+/*
+ * wan_qkv_proj_norm_rope -- the QKV projection with the Q/K RMSNorm and 3-D
+ * RoPE in its epilogue ("Optimizing High-Quality Offline Video Generation",
+ * NKI kernels: qkv_cte fuses the QKV projection, the distributed QK RMSNorm and
+ * RoPE). Computes what wan_qkv_proj followed by wan_qknorm_rope computes:
+ *   y   = bf16( x W^T + bias )                     (as wan_qkv_proj)
+ *   Q,K = the norm + RoPE of wan_qknorm_rope applied to y, V = y,
+ * without writing the unnormalised Q and K to memory. The mean square of a
+ * token's Q (and K) is summed from per-head partial sums exchanged between the
+ * output tiles of the token's block (the single-GPU counterpart of the pages'
+ * norm distributed over tensor-parallel ranks), so its fp32 summation order
+ * differs from wan_qknorm_rope's: an output can differ from the two-call
+ * result where the bf16 rounding of n_c or of the rotation sits at a tie.
+ *
+ *   x, w_qkv, bias   as wan_qkv_proj (bias may be NULL).
+ *   gamma_q, gamma_k, T, H, W, eps, theta   as wan_qknorm_rope (S = T*H*W).
+ *   qkv        bf16 [B, S, 3*D] output; must not overlap an input.
+ *   workspace  device memory of at least
+ *              wan_qkv_proj_norm_rope_workspace_bytes(B, S, heads, head_dim)
+ *              bytes, 16-byte aligned, caller-owned, overlapping no other
+ *              argument; its contents on entry do not matter. After the call
+ *              completes, the 32-bit word at byte offset 4 is nonzero if a
+ *              token block's wait for its partial sums hit the kernel's spin
+ *              limit (about a second: only when other work holds the device);
+ *              the Q and K outputs of such blocks are then NaN. Calls that
+ *              share a workspace must be ordered (same stream).
+ * Launch: a persistent grid, one workgroup per CU slot, taking output tiles
+ * from a counter in the workspace; requires room on the device for `heads`
+ * workgroups at once (WAN_E_UNSUPPORTED otherwise).
+ * Errors: as wan_qkv_proj and wan_qknorm_rope; WAN_E_NULL (workspace),
+ * WAN_E_SHAPE (workspace_bytes too small), WAN_E_ALIGN, WAN_E_ALIAS (the
+ * workspace or a gamma overlapping another buffer), WAN_E_UNSUPPORTED.
+ */
+int wan_qkv_proj_norm_rope(const void *x, const void *w_qkv, const void *bias,
+                           const void *gamma_q, const void *gamma_k, void *qkv,
+                           void *workspace, int64_t workspace_bytes,
+                           int64_t B, int64_t T, int64_t H, int64_t W,
+                           int64_t heads, int64_t head_dim,
+                           float eps, float theta, void *stream);
+
+/* Workspace bytes of wan_qkv_proj_norm_rope for B x S tokens (S = T*H*W):
+ * 256 + 4 * ceil(B*S / 256) rounded up to 256, + B*S * 2*heads * 4;
+ * -1 on invalid sizes or overflow. Pure host arithmetic. */
+int64_t wan_qkv_proj_norm_rope_workspace_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim);
 
 /*
  * wan_attn_fwd -- bidirectional multi-head softmax attention on the packed

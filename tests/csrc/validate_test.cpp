@@ -111,6 +111,48 @@ int main() {
   EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, outb, 2, 1 << 30, 2, 128, &z), WAN_E_OVERFLOW);
   EXPECT_EQ(validate_qkv_proj(buf, buf + 16384, nullptr, outb, 1, (1LL << 31) - 300, 2, 128, &z), WAN_E_ALIAS);
 
+  // Projection + norm + RoPE: x [1,16,256] at buf, w [768,256] at buf + 16384
+  // (393 KB), out [1,16,768] at outb, gammas in `other`, workspace separate.
+  // Workspace: 256 control bytes + 256 (one token block) + 16 tokens x 4 x 4 bytes.
+  FusedWorkspace fw;
+  EXPECT_EQ(fused_workspace(16, 2, &fw), 1);
+  EXPECT_EQ(fw.arrive_off, 256);
+  EXPECT_EQ(fw.partial_off, 512);
+  EXPECT_EQ(fw.bytes, 512 + 16 * 2 * 2 * 4);
+  EXPECT_EQ(fused_workspace(257, 2, &fw), 1);  // two token blocks: the counts still fit 256 bytes
+  EXPECT_EQ(fw.partial_off, 512);
+  EXPECT_EQ(fused_workspace(256 * 65, 1, &fw), 1);  // 65 token blocks: 260 bytes of counts
+  EXPECT_EQ(fw.partial_off, 256 + 512);
+  EXPECT_EQ(fused_workspace(INT64_MAX / 4, 256, &fw), 0);
+  alignas(16) static unsigned char wsb[4096];
+  const int64_t wsn = 512 + 16 * 16;
+  unsigned char* gq2 = other;
+  unsigned char* gk2 = other + 1024;
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, wsb, wsn, 1, 1, 4, 4, 2, 128, 1e-6f,
+                                        1e4f, &z), WAN_OK);
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, wsb, wsn - 1, 1, 1, 4, 4, 2, 128,
+                                        1e-6f, 1e4f, &z), WAN_E_SHAPE);
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, nullptr, wsn, 1, 1, 4, 4, 2, 128,
+                                        1e-6f, 1e4f, &z), WAN_E_NULL);
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, wsb + 8, wsn, 1, 1, 4, 4, 2, 128,
+                                        1e-6f, 1e4f, &z), WAN_E_ALIGN);
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, outb + 1024, wsn, 1, 1, 4, 4, 2,
+                                        128, 1e-6f, 1e4f, &z), WAN_E_ALIAS);  // workspace inside the output
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, buf + 32, wsn, 1, 1, 4, 4, 2, 128,
+                                        1e-6f, 1e4f, &z), WAN_E_ALIAS);  // ... inside x
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, gq2, wsn, 1, 1, 4, 4, 2, 128, 1e-6f,
+                                        1e4f, &z), WAN_E_ALIAS);  // ... on a gamma
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, outb + 64, gk2, outb, wsb, wsn, 1, 1, 4, 4, 2, 128,
+                                        1e-6f, 1e4f, &z), WAN_E_ALIAS);  // a gamma inside the output
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, wsb, wsn, 1, 1, 4, 4, 2, 128, std::nanf(""),
+                                        1e4f, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, wsb, wsn, 1, 1, 4, 4, 2, 128, 1e-6f,
+                                        -1.f, &z), WAN_E_VALUE);
+  EXPECT_EQ(validate_qkv_proj_norm_rope(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 1, 4, 4,
+                                        2, 128, 1e-6f, 1e4f, &z), WAN_OK);  // no tokens: nothing is touched
+  EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, wsb, wsn, 1, 1, 4, 4, 2, 96, 1e-6f,
+                                        1e4f, &z), WAN_E_UNSUPPORTED);
+
   // fp8 quantisation and attention
   alignas(16) static unsigned char qk8[1 << 16], vt8[1 << 16];
   alignas(16) static float sc[4], am[4];

@@ -1,0 +1,135 @@
+"""GPU parity of wan_qkv_proj_norm_rope, the projection with the Q/K RMSNorm
+and 3-D RoPE in its epilogue, through the C ABI.
+
+The fused kernel computes y = bf16(x W^T + b) with the same tiles and the same
+fp32 accumulation order as wan_qkv_proj, so
+  * its V part must equal wan_qkv_proj's V bit for bit (the projection itself
+    is pinned to the oracle by the projection tests);
+  * its Q and K must be the oracle's norm + RoPE (oracle/wan_ref.py
+    ``qknorm_rope_tokens_ref``) of wan_qkv_proj's Q and K, over EVERY token,
+    under the candidate-set rule of the norm tests (a bit may differ from the
+    oracle's nearest bf16 value only at a rounding tie; the fused mean square
+    is summed from per-head partial sums, in another fp32 order than the
+    in-place norm's).
+Shapes: one token, ragged token blocks, odd head counts (a tile straddling K
+and V), several token blocks at the full 40-head width, and the full 480p
+workload in the launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from tests.parity import norm_rope_full_parity
+from video_diffusion_transformer_amd import synth, wan_attn
+from video_diffusion_transformer_amd.configs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _inputs(B, grid, heads, seed, device="cpu"):
+    T, H, W = grid
+    D = heads * 128
+    x = synth.make_tokens(B, T * H * W, D, seed=seed, device=device).to(DEV)
+    w, b = (t.to(DEV) for t in synth.make_qkv_weights(D, seed=seed))
+    gq, gk = synth.make_gammas(D, seed=seed, device=DEV)
+    return x, w, b, gq, gk
+
+
+def _check(x, w, b, gq, gk, grid, heads, what, bias=True):
+    D = heads * 128
+    out, ws = wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, bias=b if bias else None)
+    y = wan_attn.qkv_proj(x, w, heads, bias=b if bias else None)
+    torch.cuda.synchronize()
+    assert wan_attn.proj_norm_rope_error_word(ws) == 0, what
+    M = x.shape[0] * x.shape[1]
+    o, yy = out.view(M, 3 * D), y.view(M, 3 * D)
+    assert torch.equal(o[:, 2 * D:], yy[:, 2 * D:]), f"{what}: V differs from the projection's"
+    res = norm_rope_full_parity(yy.cpu(), o.cpu(), gq.double().cpu().numpy(), gk.double().cpu().numpy(), grid,
+                                heads)
+    assert res["bad"] == 0, f"{what}: {res['bad']} Q/K outputs outside the candidate sets"
+    assert res["exact"] >= 0.999, f"{what}: only {res['exact']:.5f} equal to the oracle's nearest value"
+    return out, y, res
+
+
+@pytest.mark.parametrize("B,grid,heads", [(1, (1, 1, 1), 1), (1, (2, 8, 8), 2), (2, (3, 5, 7), 3),
+                                          (1, (2, 9, 15), 5), (2, (3, 10, 20), 40)])
+def test_small_every_token(B, grid, heads):
+    x, w, b, gq, gk = _inputs(B, grid, heads, seed=sum(grid) + heads)
+    _check(x, w, b, gq, gk, grid, heads, f"B{B} {grid} h{heads}")
+
+
+def test_without_bias_and_repeat_calls():
+    """No bias; two calls in a row on one workspace (its counters are cleared
+    by each call) give the same bits; a call on a smaller input after a larger
+    one is still correct."""
+    grid, heads = (2, 12, 13), 4
+    x, w, b, gq, gk = _inputs(1, grid, heads, seed=11)
+    out1, ws = wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads)
+    out2, _ = wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    _check(x, w, None, gq, gk, grid, heads, "no bias", bias=False)
+    small = (1, 3, 5)
+    xs = x[:, :15].contiguous()
+    out3, _ = wan_attn.qkv_proj_norm_rope(xs, w, gq, gk, small, heads, workspace=ws)
+    y3 = wan_attn.qkv_proj(xs, w, heads)
+    torch.cuda.synchronize()
+    assert wan_attn.proj_norm_rope_error_word(ws) == 0
+    D = heads * 128
+    res = norm_rope_full_parity(y3.view(15, 3 * D).cpu(), out3.view(15, 3 * D).cpu(), gq.double().cpu().numpy(),
+                                gk.double().cpu().numpy(), small, heads)
+    assert res["bad"] == 0
+
+
+def test_matches_two_call_path_bits_mostly():
+    """Against the two-call GPU path (projection, then norm + RoPE in place):
+    V equal everywhere, Q and K equal except at rounding ties of the norm."""
+    grid, heads = (2, 16, 16), 40
+    x, w, b, gq, gk = _inputs(1, grid, heads, seed=21)
+    out, _ = wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, bias=b)
+    two = wan_attn.qkv_proj(x, w, heads, bias=b)
+    wan_attn.qknorm_rope(two, gq, gk, grid, heads)
+    torch.cuda.synchronize()
+    eq = (out == two).float().mean().item()
+    assert eq >= 0.999, eq
+    D = heads * 128
+    assert torch.equal(out[..., 2 * D:], two[..., 2 * D:])
+
+
+def test_full_480p_every_token():
+    """The 480p workload (B = 2, 32,760 tokens, 40 heads: 256 token blocks x 60
+    feature tiles on a persistent grid) in the benchmark's launch
+    configuration: V bit-equal to the projection's, every Q and K output
+    against the oracle's norm + RoPE of the projection's Q and K."""
+    wl = WORKLOADS["480p"]
+    grid = (wl.T, wl.H, wl.W)
+    x = synth.make_tokens(wl.B, wl.S, wl.D, seed=wl.seed, device=DEV)
+    w, b = synth.make_qkv_weights(wl.D, seed=wl.seed, device=DEV)
+    gq, gk = synth.make_gammas(wl.D, seed=wl.seed, device=DEV)
+    _, _, res = _check(x, w, b, gq, gk, grid, wl.heads, "480p")
+    print(f"480p fused projection + norm + RoPE: exact {res['exact']:.6f}, max err {res['max']:.3g}")
+
+
+def test_errors_and_empty():
+    grid, heads = (1, 2, 4), 2
+    x, w, b, gq, gk = _inputs(1, grid, heads, seed=3)
+    need = wan_attn.qkv_proj_norm_rope_workspace_bytes(1, 8, heads)
+    small = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
+    with pytest.raises(wan_attn.WanError) as e:
+        wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, workspace=small)
+    assert e.value.status == -2
+    out = torch.empty((1, 8, 3 * heads * 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(wan_attn.WanError) as e:  # workspace inside the output
+        wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, out=out,
+                                    workspace=out.view(torch.uint8).view(-1)[:need])
+    assert e.value.status == -5
+    with pytest.raises(wan_attn.WanError) as e:
+        wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, eps=float("nan"))
+    assert e.value.status == -9
+    empty = torch.empty((0, 8, heads * 128), dtype=torch.bfloat16, device=DEV)
+    o, _ = wan_attn.qkv_proj_norm_rope(empty, w, gq, gk, grid, heads,
+                                       workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert o.shape == (0, 8, 3 * heads * 128)

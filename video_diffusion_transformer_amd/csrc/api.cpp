@@ -101,6 +101,33 @@ int wan_qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, 
   return WAN_OK;
 }
 
+int64_t wan_qkv_proj_norm_rope_workspace_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim) {
+  wan::Sizes z;
+  if (wan::check_sizes(B, S, heads, head_dim, &z) != WAN_OK) return -1;
+  wan::FusedWorkspace f;
+  if (!wan::fused_workspace(z.rows, heads, &f)) return -1;
+  return f.bytes;
+}
+
+int wan_qkv_proj_norm_rope(const void* x, const void* w_qkv, const void* bias, const void* gamma_q,
+                           const void* gamma_k, void* qkv, void* workspace, int64_t workspace_bytes, int64_t B,
+                           int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
+                           void* stream) {
+  wan::Sizes z;
+  int rc = wan::validate_qkv_proj_norm_rope(x, w_qkv, bias, gamma_q, gamma_k, qkv, workspace, workspace_bytes, B, T,
+                                            H, W, heads, head_dim, eps, theta, &z);
+  if (rc != WAN_OK || z.empty) return rc;
+  auto st = static_cast<hipStream_t>(stream);
+  const float2* tab = nullptr;
+  rc = rope_table(T, H, W, theta, st, &tab);
+  if (rc != WAN_OK) return rc;
+  const hipError_t e = wan::launch_qkv_proj_norm_rope(
+      x, w_qkv, bias, gamma_q, gamma_k, tab, qkv, workspace, z.rows, static_cast<int>(heads), static_cast<int>(z.S),
+      static_cast<int>(T), static_cast<int>(H), static_cast<int>(W), eps, st);
+  if (e == hipErrorInvalidConfiguration) return WAN_E_UNSUPPORTED;
+  return e == hipSuccess ? WAN_OK : WAN_E_HIP;
+}
+
 int wan_qknorm_rope(void* qkv, const void* gamma_q, const void* gamma_k, int64_t B, int64_t T,
                     int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
                     void* stream) {

@@ -68,6 +68,17 @@ hipError_t launch_quant_v_delayed(const void* qkv, void* vt8, const float* amax_
 hipError_t launch_qkv_proj(const void* x, const void* w, const void* bias, void* out, int64_t M, int N, int K,
                            hipStream_t stream);
 
+// The projection of M = B * S tokens with the Q/K RMSNorm and 3-D RoPE in its
+// epilogue (D = heads * 128; out [M, 3D] holds normalised, rotated Q and K and
+// plain V). workspace: fused_workspace(M, heads) bytes (validate.hpp), its
+// counters cleared by the launch itself (word 1 is nonzero afterwards if a
+// token block's wait hit its spin limit). Fails with
+// hipErrorInvalidConfiguration when the device cannot hold `heads` workgroups
+// of the kernel at once.
+hipError_t launch_qkv_proj_norm_rope(const void* x, const void* w, const void* bias, const void* gq, const void* gk,
+                                     const float2* tab, void* out, void* workspace, int64_t M, int heads, int S, int T,
+                                     int H, int W, float eps, hipStream_t stream);
+
 // fp8 attention forward from the quantised buffers.
 hipError_t launch_attn_fwd_fp8(const void* qk8, const void* vt8, const float* scales, void* out, float* lse, int B,
                                int S, int heads, float softmax_scale, hipStream_t stream);

@@ -31,14 +31,18 @@
 //     sweeping the feature tiles, so the ~32 workgroups an XCD runs at once
 //     share 8 x tiles and 4 W tiles in its L2 (groups of 16 or 32 token tiles
 //     measured 10% and 20% slower).
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
+#include "validate.hpp"
 
 namespace wan {
 
 namespace {
 
 constexpr int kPM = 256, kPN = 256, kPK = 64;  // tile: tokens, features, channels per step
+static_assert(kPM == kFusedTileTokens && kPN == kFusedTileFeatures, "workspace layout follows the tile");
 constexpr int kPWaves = 8, kPThreads = 64 * kPWaves;
 constexpr int kPRow = kPK * 2;                 // bytes per LDS row
 constexpr int kPTile = kPM * kPRow;            // 32 KB per operand tile
@@ -68,23 +72,13 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__global__ void __launch_bounds__(kPThreads, 1)
-qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-                uint16_t* __restrict__ out, int M, int N, int K, int ntm, int ntn) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kPStage];
-
-  // Tile order: XCD-major, then groups of kPGroup token tiles x all feature tiles.
-  const int lid = p_xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = kPGroup * ntn;
-  const int group = lid / per_group;
-  const int first_tm = group * kPGroup;
-  const int gm = min(ntm - first_tm, kPGroup);
-  const int rr = lid - group * per_group;
-  const int tm = first_tm + rr % gm, tn = rr / gm;
-  const int m0 = tm * kPM, n0 = tn * kPN;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// The 256 x 256 tile (m0, n0) of x W^T (no bias) into acc: each lane ends with
+// 4 consecutive features of one token per MFMA tile (i, j) -- features
+// n0 + 128 wn + 16 i + 4 grp .. +3 of token m0 + 64 wm + 16 j + l16. On return
+// every wave has left the LDS stages (the caller may reuse the LDS).
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int N,
+                                          int K, int m0, int n0, unsigned char* __restrict__ smem, int wave, int lane,
+                                          f32x4_t (&acc)[8][4]) {
   const int l16 = lane & 15, grp = lane >> 4;
   const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves: features 128 wn.., tokens 64 wm..
 
@@ -120,7 +114,6 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
 #pragma unroll
   for (int s = 0; s < 2; ++s) roff[s] = l16 * kPRow + 16 * ((4 * s + grp) ^ p_swz(l16));
 
-  f32x4_t acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -177,39 +170,31 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
   // the epilogue reuses the LDS.
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
+}
 
-  // Epilogue through LDS (free after the last barrier): each wave writes its
-  // 64 tokens x 128 features, bias added and rounded to bf16, into its own 16 KB
-  // (one 256-byte row per token), then stores whole 16-byte pieces of rows, so
-  // a store instruction covers 4 tokens x 256 contiguous bytes instead of 16
-  // tokens x 32 bytes. Lane (l16, grp) of tile (i, j) holds features
-  // 16 i + 4 grp .. +3 of token 16 j + l16. The 8-byte unit u of a row is
-  // stored at u ^ f(row), f(row) = 2 ((row >> 1) & 15): even, so 16-byte
-  // pieces stay whole, and the writes of a half-wave (16 rows x 2 units) and
-  // the reads (2 rows x 256 bytes) both cover distinct banks.
+// Epilogue through LDS (free after gemm_tile): each wave writes its 64 tokens x
+// 128 features, as the packed bf16 pairs pk(i, j) returns for MFMA tile (i, j),
+// into its own 16 KB (one 256-byte row per token), then stores whole 16-byte
+// pieces of rows, so a store instruction covers 4 tokens x 256 contiguous bytes
+// instead of 16 tokens x 32 bytes. The 8-byte unit u of a row is stored at
+// u ^ f(row), f(row) = 2 ((row >> 1) & 15): even, so 16-byte pieces stay whole,
+// and the writes of a half-wave (16 rows x 2 units) and the reads (2 rows x 256
+// bytes) both cover distinct banks.
+template <class Pack>
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, int M, int N, int m0, int n0,
+                                           unsigned char* __restrict__ smem, int wave, int lane, Pack pk) {
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
   unsigned char* ep = smem + wave * (64 * 256);
   const int nb = n0 + 128 * wn;  // first feature of this wave's tile
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    const int n = nb + 16 * i + 4 * grp;
-    if (bias && n < N) {
-      const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
-      bv[0] = bf16_lo(bw.x);
-      bv[1] = bf16_hi(bw.x);
-      bv[2] = bf16_lo(bw.y);
-      bv[3] = bf16_hi(bw.y);
-    }
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 16 * j + l16;
       const int u = (4 * i + grp) ^ (((row >> 1) & 15) << 1);
-      uint2 o;
-      o.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
-      o.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
-      *reinterpret_cast<uint2*>(ep + row * 256 + u * 8) = o;
+      *reinterpret_cast<uint2*>(ep + row * 256 + u * 8) = pk(i, j);
     }
-  }
   // Each wave reads back only what it wrote: the compiler's LDS waits order it.
   const int k = lane & 15;  // 16-byte piece: features nb + 8 k .. +7
 #pragma unroll
@@ -218,6 +203,232 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + row * 256 + ((2 * k) ^ (((row >> 1) & 15) << 1)) * 8);
     const int m = m0 + 64 * wm + row, n = nb + 8 * k;
     if (m < M && n < N) *reinterpret_cast<u32x4_t*>(out + (int64_t)m * N + n) = v;
+  }
+}
+
+// Bias of the 4 features n .. n+3 (zero without bias or past N).
+__device__ __forceinline__ void load_bias4(const uint16_t* __restrict__ bias, int n, int N, float (&bv)[4]) {
+  bv[0] = bv[1] = bv[2] = bv[3] = 0.f;
+  if (bias && n < N) {
+    const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
+    bv[0] = bf16_lo(bw.x);
+    bv[1] = bf16_hi(bw.x);
+    bv[2] = bf16_lo(bw.y);
+    bv[3] = bf16_hi(bw.y);
+  }
+}
+
+__global__ void __launch_bounds__(kPThreads, 1)
+qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+                uint16_t* __restrict__ out, int M, int N, int K, int ntm, int ntn) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kPStage];
+
+  // Tile order: XCD-major, then groups of kPGroup token tiles x all feature tiles.
+  const int lid = p_xcd_remap(blockIdx.x, gridDim.x);
+  const int per_group = kPGroup * ntn;
+  const int group = lid / per_group;
+  const int first_tm = group * kPGroup;
+  const int gm = min(ntm - first_tm, kPGroup);
+  const int rr = lid - group * per_group;
+  const int tm = first_tm + rr % gm, tn = rr / gm;
+  const int m0 = tm * kPM, n0 = tn * kPN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4, wn = wave & 1;
+
+  f32x4_t acc[8][4];
+  gemm_tile(x, w, M, N, K, m0, n0, smem, wave, lane, acc);
+
+  // Bias added in fp32, one rounding to bf16.
+  const int nb = n0 + 128 * wn;
+  float bv[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_bias4(bias, nb + 16 * i + 4 * grp, N, bv[i]);
+  store_tile(out, M, N, m0, n0, smem, wave, lane, [&](int i, int j) {
+    uint2 o;
+    o.x = pack_bf16x2(acc[i][j][0] + bv[i][0], acc[i][j][1] + bv[i][1]);
+    o.y = pack_bf16x2(acc[i][j][2] + bv[i][2], acc[i][j][3] + bv[i][3]);
+    return o;
+  });
+}
+
+// ---------------------------------------------------------------------------
+// The projection with the Q/K RMSNorm and 3-D RoPE in its epilogue (the qkv_cte
+// kernel of "Optimizing High-Quality Offline Video Generation", NKI kernels: QKV
+// projection, distributed QK RMSNorm and RoPE in one kernel). A token's norm
+// spans all D channels of its Q (and of its K): `heads` wave columns of 128
+// features each, spread over heads / 2 output tiles. As the pages distribute
+// the norm over the tensor-parallel ranks that hold the head shards, the tiles
+// of one token block exchange per-token partial sums of squares: each tile
+// rounds its outputs to bf16 (the projection's own rounding point), publishes
+// every token's sum of squares over each of its 128-feature wave columns, waits
+// until all Q and K columns of its token block have published, and then
+// normalises, rotates and rounds its tile in registers. The unnormalised Q and
+// K never reach memory.
+//
+// Scheduling: a persistent grid (one workgroup per CU slot) takes tiles from an
+// atomic counter in token-block order (token block, then feature tile). A
+// workgroup publishes before it waits and waits only for the Q/K tiles of its
+// own token block. Waiting workgroups hold Q/K tiles of the lowest unfinished
+// token block only (every tile of a lower block has been taken and published),
+// so at most heads - 1 wait at once (some Q/K tile of that block is still
+// untaken); with room on the device for `heads` workgroups, some workgroup is
+// always free to take the missing tiles, and every wait ends. A bounded spin guards the rest (e.g. the device held by
+// other work): past the limit the workgroup sets the error word of the
+// workspace and stores NaN bits for its Q and K outputs.
+// ---------------------------------------------------------------------------
+constexpr int kPairsT = 22, kPairsH = 21, kPairsW = 21;  // rotary pairs per axis (44/42/42 channels)
+constexpr unsigned kSpinLimit = 1u << 20;                // polls of a token block's arrival count (about 1 s)
+
+struct NormRopeArgs {
+  const uint16_t* gq;  // RMSNorm weights of Q and of K, [D] bf16
+  const uint16_t* gk;
+  const float2* tab;   // rotary (cos, sin): frame [T][22], row [H][21], column [W][21]
+  int S, H, W, offH, offW, heads;
+  float inv_d, eps;
+  unsigned* ctl;       // [0] tile counter, [1] error word (a wait hit the spin limit)
+  unsigned* arrive;    // [ntm] published Q/K wave columns per token block
+  float* partial;      // [M][2 heads] sums of squares per token and wave column (Q heads, then K heads)
+};
+
+__global__ void __launch_bounds__(256) zero_u32_kernel(unsigned* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ void __launch_bounds__(kPThreads, 1)
+qkv_proj_norm_rope_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N, int K, int ntm,
+                          int ntn, NormRopeArgs na) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kPStage];
+  __shared__ int tile_sh, late_sh;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int D = na.heads * 128;
+  const int slots = 2 * na.heads;  // Q and K wave columns of a token block
+  const int ntiles = ntm * ntn;
+
+  for (;;) {
+    // The barrier at the end of the previous tile orders this write after every read of tile_sh.
+    if (tid == 0) tile_sh = static_cast<int>(atomicAdd(na.ctl, 1u));
+    __syncthreads();
+    const int t = tile_sh;
+    if (t >= ntiles) break;
+    const int tm = t / ntn, tn = t - tm * ntn;
+    const int m0 = tm * kPM, n0 = tn * kPN;
+
+    f32x4_t acc[8][4];
+    gemm_tile(x, w, M, N, K, m0, n0, smem, wave, lane, acc);
+
+    // y = bf16(x W^T + b): the values the packed buffer of the plain projection holds.
+    const int nb = n0 + 128 * wn;  // this wave's first feature (a multiple of 128: inside one of Q, K, V)
+    const int part = nb / D;       // 0 Q, 1 K, 2 V
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float bv[4];
+      load_bias4(bias, nb + 16 * i + 4 * grp, N, bv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = static_cast<float>(static_cast<__bf16>(acc[i][j][e] + bv[e]));
+    }
+
+    // Q/K wave columns in this tile (0, 1 or 2); whether this wave holds one.
+    const int qk_cols = (n0 < N && n0 / D < 2 ? 1 : 0) + (n0 + 128 < N && (n0 + 128) / D < 2 ? 1 : 0);
+    const bool qk = nb < N && part < 2;
+    if (qk_cols > 0) {
+      if (qk) {
+        // Sum of squares of each of the wave's 64 tokens over its 128 features.
+        const int slot = part * na.heads + (nb - part * D) / 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float ss = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += acc[i][j][e] * acc[i][j][e];
+          ss += __shfl_xor(ss, 16, 64);
+          ss += __shfl_xor(ss, 32, 64);
+          const int m = m0 + 64 * wm + 16 * j + l16;
+          if (grp == 0 && m < M) na.partial[(int64_t)m * slots + slot] = ss;
+        }
+        __threadfence();  // release: the partial sums are visible device-wide before the arrival below
+      }
+      __syncthreads();
+      if (tid == 0) {
+        atomicAdd(na.arrive + tm, static_cast<unsigned>(qk_cols));
+        unsigned spins = 0;
+        int late = 0;
+        while (__hip_atomic_load(na.arrive + tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               static_cast<unsigned>(slots)) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > kSpinLimit) {
+            atomicOr(na.ctl + 1, 1u);
+            late = 1;
+            break;
+          }
+        }
+        __threadfence();  // acquire: the other columns' partial sums are read after this point
+        late_sh = late;
+      }
+      __syncthreads();
+    }
+
+    // A timed-out wait leaves the norm unknown: its Q/K outputs are stored as NaN bits.
+    const bool bad = qk && qk_cols > 0 && late_sh != 0;
+    if (qk) {
+      const uint16_t* g = part == 0 ? na.gq : na.gk;
+      const int cbase = nb - part * D;  // channel of this wave's first feature within Q or K
+      float r[4];                       // (mean square + eps)^-1/2 of the wave's tokens 16 j + l16
+      int f_[4], y_[4], x_[4];          // their (frame, row, column) on the token grid
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = min(m0 + 64 * wm + 16 * j + l16, M - 1);  // rows past M: any valid row (not stored)
+        const float* pr = na.partial + (int64_t)m * slots + part * na.heads;
+        float ss = 0.f;
+        for (int c = grp; c < na.heads; c += 4) ss += pr[c];
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        r[j] = rsqrtf(ss * na.inv_d + na.eps);
+        const int s = m % na.S;
+        f_[j] = s / (na.H * na.W);
+        y_[j] = (s / na.W) % na.H;
+        x_[j] = s % na.W;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = cbase + 16 * i + 4 * grp;  // channels c .. c+3 of Q (or K): rotary pairs p0, p0 + 1
+        const uint2 gw = *reinterpret_cast<const uint2*>(g + c);
+        const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
+        const int p0 = (c & 127) >> 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int p = p0 + h;
+            const float2 cs = p < kPairsT ? na.tab[f_[j] * kPairsT + p]
+                                          : (p < kPairsT + kPairsH ? na.tab[na.offH + y_[j] * kPairsH + (p - kPairsT)]
+                                                                   : na.tab[na.offW + x_[j] * kPairsW + (p - kPairsT - kPairsH)]);
+            // norm, x gamma, bf16 rounding point; rotation in fp32 (bf16 at the store)
+            const uint32_t nv = pack_bf16x2(acc[i][j][2 * h] * r[j] * gv[2 * h], acc[i][j][2 * h + 1] * r[j] * gv[2 * h + 1]);
+            const float a = bf16_lo(nv), b = bf16_hi(nv);
+            acc[i][j][2 * h] = a * cs.x - b * cs.y;
+            acc[i][j][2 * h + 1] = a * cs.y + b * cs.x;
+          }
+        }
+      }
+    }
+    store_tile(out, M, N, m0, n0, smem, wave, lane, [&](int i, int j) {
+      uint2 o;
+      o.x = bad ? 0x7fc07fc0u : pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+      o.y = bad ? 0x7fc07fc0u : pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      return o;
+    });
+    __syncthreads();  // the epilogue's LDS is the next tile's staging, and tile_sh is rewritten
   }
 }
 
@@ -236,6 +447,72 @@ hipError_t launch_qkv_proj(const void* x, const void* w, const void* bias, void*
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
                      static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), static_cast<int>(M), N, K,
                      static_cast<int>(ntm), ntn);
+  return hipGetLastError();
+}
+
+}  // namespace wan
+
+namespace wan {
+
+// Workgroups of the fused kernel the device holds at once (cached per device).
+static int fused_capacity(int dev) {
+  static std::mutex mu;
+  static int cap[64] = {};
+  if (dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cap[dev]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, qkv_proj_norm_rope_kernel, kPThreads, 0) != hipSuccess)
+      return 0;
+    cap[dev] = cus * per_cu;
+  }
+  return cap[dev];
+}
+
+hipError_t launch_qkv_proj_norm_rope(const void* x, const void* w, const void* bias, const void* gq, const void* gk,
+                                     const float2* tab, void* out, void* workspace, int64_t M, int heads, int S, int T,
+                                     int H, int W, float eps, hipStream_t stream) {
+  const int D = heads * 128, N = 3 * D, K = D;
+  const int64_t ntm = (M + kPM - 1) / kPM;
+  const int ntn = (N + kPN - 1) / kPN;
+  if (ntm * ntn > INT32_MAX / 2 || (int64_t)kPM * K * 2 > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int cap = fused_capacity(dev);
+  // At most heads - 1 workgroups wait at once; one more must fit for every wait to end.
+  if (cap < heads) return hipErrorInvalidConfiguration;
+  const int ntiles = static_cast<int>(ntm * ntn);
+  const int grid = cap < ntiles ? cap : ntiles;
+  FusedWorkspace fw;
+  if (!fused_workspace(M, heads, &fw)) return hipErrorInvalidValue;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  NormRopeArgs na;
+  na.gq = static_cast<const uint16_t*>(gq);
+  na.gk = static_cast<const uint16_t*>(gk);
+  na.tab = tab;
+  na.S = S;
+  na.H = H;
+  na.W = W;
+  na.offH = T * kPairsT;
+  na.offW = na.offH + H * kPairsH;
+  na.heads = heads;
+  na.inv_d = 1.0f / static_cast<float>(D);
+  na.eps = eps;
+  na.ctl = reinterpret_cast<unsigned*>(ws);
+  na.arrive = reinterpret_cast<unsigned*>(ws + fw.arrive_off);
+  na.partial = reinterpret_cast<float*>(ws + fw.partial_off);
+  // Counters and error word start at zero: a fill kernel (no memset node if the call is captured in a graph).
+  const int64_t nz = 64 + ntm;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(static_cast<unsigned>((nz + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<unsigned*>(ws), nz);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qkv_proj_norm_rope_kernel, dim3(grid), dim3(kPThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                     static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), static_cast<int>(M), N, K,
+                     static_cast<int>(ntm), ntn, na);
   return hipGetLastError();
 }
 

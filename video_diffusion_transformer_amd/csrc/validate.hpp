@@ -215,6 +215,57 @@ inline int validate_qkv_proj(const void* x, const void* w, const void* bias, con
   return WAN_OK;
 }
 
+// Workspace of the projection with the norm + RoPE epilogue, for `rows` tokens
+// and `heads` heads: 256 bytes of control words (tile counter, error word), one
+// 32-bit arrival count per 256-token block (the span rounded up to 256 bytes),
+// then rows x 2 heads fp32 partial sums of squares. False on overflow.
+struct FusedWorkspace {
+  int64_t arrive_off, partial_off, bytes;
+};
+constexpr int64_t kFusedTileTokens = 256, kFusedTileFeatures = 256;
+inline bool fused_workspace(int64_t rows, int64_t heads, FusedWorkspace* f) {
+  if (rows < 0 || heads < 1 || rows > INT64_MAX / 4 - kFusedTileTokens) return false;
+  const int64_t ntm = (rows + kFusedTileTokens - 1) / kFusedTileTokens;
+  int64_t part;
+  if (!mul_ok(rows, 8 * heads, &part)) return false;
+  f->arrive_off = 256;
+  f->partial_off = 256 + (4 * ntm + 255) / 256 * 256;
+  if (part > INT64_MAX - f->partial_off) return false;
+  f->bytes = f->partial_off + part;
+  return true;
+}
+
+// Projection + norm + RoPE: the norm checks on the output buffer (grid, eps,
+// theta, gammas), the projection checks (x, w, bias against the output), a
+// workspace of at least fused_workspace() bytes, 16-byte aligned, overlapping
+// no other buffer, and a tile count within 32 bits.
+inline int validate_qkv_proj_norm_rope(const void* x, const void* w, const void* bias, const void* gq, const void* gk,
+                                       const void* out, const void* ws, int64_t ws_bytes, int64_t B, int64_t T,
+                                       int64_t H, int64_t W, int64_t heads, int64_t head_dim, float eps, float theta,
+                                       Sizes* z) {
+  int rc = validate_qknorm_rope(out, gq, gk, B, T, H, W, heads, head_dim, eps, theta, z);
+  if (rc != WAN_OK) return rc;
+  rc = validate_qkv_proj(x, w, bias, out, B, z->S, heads, head_dim, z);
+  if (rc != WAN_OK || z->empty) return rc;
+  if (T > INT32_MAX / 22 || H > INT32_MAX / 21 || W > INT32_MAX / 21) return WAN_E_OVERFLOW;
+  const int64_t ntm = (z->rows + kFusedTileTokens - 1) / kFusedTileTokens;
+  const int64_t ntn = (3 * z->D + kFusedTileFeatures - 1) / kFusedTileFeatures;
+  if (ntm > INT32_MAX / 2 / ntn) return WAN_E_OVERFLOW;
+  FusedWorkspace f;
+  if (!fused_workspace(z->rows, heads, &f)) return WAN_E_OVERFLOW;
+  if (!ws) return WAN_E_NULL;
+  if (!aligned(ws, 16)) return WAN_E_ALIGN;
+  if (ws_bytes < f.bytes) return WAN_E_SHAPE;
+  const void* p[6] = {x, w, bias, gq, gk, out};
+  const int64_t n[6] = {z->out_elems * 2, 3 * z->D * z->D * 2, 3 * z->D * 2, z->D * 2, z->D * 2, z->qkv_elems * 2};
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(ws, f.bytes, p[i], n[i])) return WAN_E_ALIAS;
+  // the gammas are read while the output is written
+  if (overlaps(gq, z->D * 2, out, z->qkv_elems * 2) || overlaps(gk, z->D * 2, out, z->qkv_elems * 2))
+    return WAN_E_ALIAS;
+  return WAN_OK;
+}
+
 // Bytes of the transposed fp8 V buffer: B * heads * 128 * S_pad, S_pad = S rounded up to 128.
 inline bool fp8_vt_bytes(int64_t B, int64_t S, int64_t heads, int64_t* out) {
   if (S < 0 || S > INT64_MAX - 127) return false;

@@ -6,7 +6,7 @@ live on the GPU; there is no CPU path. If the library is not built the first
 call raises -- nothing falls back to another implementation.
 
 The names follow the C ABI: ``token_grid`` -> wan_token_grid, ``qkv_proj`` -> wan_qkv_proj,
-``qknorm_rope`` -> wan_qknorm_rope, ``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_skip`` -> wan_attn_fwd_skip,
+``qknorm_rope`` -> wan_qknorm_rope, ``qkv_proj_norm_rope`` -> wan_qkv_proj_norm_rope, ``attn_fwd`` -> wan_attn_fwd, ``attn_fwd_skip`` -> wan_attn_fwd_skip,
 ``attn_fwd_chunk`` -> wan_attn_fwd_chunk, ``attn_merge`` -> wan_attn_merge,
 ``attn_fwd_chunk_merge`` -> wan_attn_fwd_chunk_merge,
 ``qkv_quant_fp8`` -> wan_qkv_quant_fp8,
@@ -42,6 +42,9 @@ SIGNATURES = {
                                       ctypes.POINTER(_I64)]),
     "wan_qkv_proj": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "wan_qknorm_rope": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
+    "wan_qkv_proj_norm_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                              _F, _F, _P]),
+    "wan_qkv_proj_norm_rope_workspace_bytes": (ctypes.c_int64, [_I64, _I64, _I64, _I64]),
     "wan_qknorm_rope_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _F, _P]),
     "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _F, _P]),
     "wan_attn_fwd_skip": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _F, _P]),
@@ -158,6 +161,53 @@ def qknorm_rope(qkv, gamma_q, gamma_k, grid, heads, head_dim=HEAD_DIM, eps=RMS_E
             _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), B, T, H, W, heads, head_dim, eps, theta,
             _stream(qkv.device, stream)))
     return qkv
+
+
+def qkv_proj_norm_rope_workspace_bytes(B, S, heads, head_dim=HEAD_DIM):
+    n = lib().wan_qkv_proj_norm_rope_workspace_bytes(B, S, heads, head_dim)
+    if n < 0:
+        raise ValueError("invalid sizes for the projection + norm + RoPE workspace")
+    return n
+
+
+def qkv_proj_norm_rope(x, w_qkv, gamma_q, gamma_k, grid, heads, bias=None, head_dim=HEAD_DIM, eps=RMS_EPS,
+                       theta=ROPE_THETA, out=None, workspace=None, stream=None):
+    """Packed [B, S, 3D] bf16 of the projection x w_qkv^T (+ bias) with the Q/K
+    RMSNorm + 3-D RoPE applied in the epilogue (S = T*H*W). ``workspace`` is a
+    uint8 device tensor of at least qkv_proj_norm_rope_workspace_bytes(B, S,
+    heads) bytes (allocated when None). Returns (out, workspace); byte 4..7 of
+    the workspace is the error word (nonzero after a wait hit its spin limit)."""
+    T, H, W = grid
+    D = heads * head_dim
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        _need_gpu(name, t, torch.bfloat16)
+    if bias is not None:
+        _need_gpu("bias", bias, torch.bfloat16)
+        if bias.numel() != 3 * D:
+            raise ValueError("bias must have 3*heads*head_dim elements")
+    if x.dim() != 3 or x.shape[1] != T * H * W or x.shape[2] != D or tuple(w_qkv.shape) != (3 * D, D):
+        raise ValueError(f"x must be [B, {T * H * W}, {D}] and w_qkv [3*D, D]")
+    if gamma_q.numel() != D or gamma_k.numel() != D:
+        raise ValueError("gammas must have heads*head_dim elements")
+    B, S = x.shape[0], x.shape[1]
+    out = torch.empty((B, S, 3 * D), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need_gpu("out", out, torch.bfloat16)
+    if tuple(out.shape) != (B, S, 3 * D):
+        raise ValueError("out must be [B, S, 3*D]")
+    if workspace is None:
+        workspace = torch.empty(qkv_proj_norm_rope_workspace_bytes(B, S, heads, head_dim), dtype=torch.uint8,
+                                device=x.device)
+    _need_gpu("workspace", workspace, torch.uint8)
+    with torch.cuda.device(x.device):
+        _check("wan_qkv_proj_norm_rope", lib().wan_qkv_proj_norm_rope(
+            _ptr(x), _ptr(w_qkv), _ptr(bias), _ptr(gamma_q), _ptr(gamma_k), _ptr(out), _ptr(workspace),
+            workspace.numel(), B, T, H, W, heads, head_dim, eps, theta, _stream(x.device, stream)))
+    return out, workspace
+
+
+def proj_norm_rope_error_word(workspace):
+    """The workspace's error word (synchronises with the device)."""
+    return int(workspace[4:8].view(torch.int32).item())
 
 
 def attn_fwd(qkv, heads, head_dim=HEAD_DIM, softmax_scale=None, out=None, lse=False, stream=None):
