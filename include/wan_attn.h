@@ -123,9 +123,12 @@ int wan_token_grid(int64_t width, int64_t height, int64_t num_frames, int64_t *T
  *          input.
  * Arithmetic: bf16 products accumulated in fp32 (gfx950 MFMA), bias added in
  * fp32, one round-to-nearest-even to bf16.
+ * Launch: a persistent grid taking output tiles from a 16-byte device counter
+ * that the library allocates on the first call per (device, stream) and keeps
+ * until the process ends; calls on one stream share it in stream order.
  * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN (16-byte),
  * WAN_E_ALIAS, WAN_E_OVERFLOW (also B*S above 2^31 - 257 token rows),
- * WAN_E_HIP.
+ * WAN_E_NOMEM (the counter), WAN_E_HIP.
  */
 int wan_qkv_proj(const void *x, const void *w_qkv, const void *bias, void *qkv, int64_t B, int64_t S,
                  int64_t heads, int64_t head_dim, void *stream);
@@ -208,7 +211,7 @@ int wan_qkv_proj_norm_rope(const void *x, const void *w_qkv, const void *bias,
                            float eps, float theta, void *stream);
 
 /* Workspace bytes of wan_qkv_proj_norm_rope for B x S tokens (S = T*H*W):
- * 256 + 4 * ceil(B*S / 256) rounded up to 256, + B*S * 2*heads * 4;
+ * 256 + 8 * ceil(B*S / 256) rounded up to 256, + B*S * 2*heads * 8;
  * -1 on invalid sizes or overflow. Pure host arithmetic. */
 int64_t wan_qkv_proj_norm_rope_workspace_bytes(int64_t B, int64_t S, int64_t heads, int64_t head_dim);
 

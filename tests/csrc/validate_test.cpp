@@ -113,19 +113,19 @@ int main() {
 
   // Projection + norm + RoPE: x [1,16,256] at buf, w [768,256] at buf + 16384
   // (393 KB), out [1,16,768] at outb, gammas in `other`, workspace separate.
-  // Workspace: 256 control bytes + 256 (one token block) + 16 tokens x 4 x 4 bytes.
+  // Workspace: 256 control bytes + 256 (one token block) + 16 tokens x 4 x 8 bytes.
   FusedWorkspace fw;
   EXPECT_EQ(fused_workspace(16, 2, &fw), 1);
   EXPECT_EQ(fw.arrive_off, 256);
   EXPECT_EQ(fw.partial_off, 512);
-  EXPECT_EQ(fw.bytes, 512 + 16 * 2 * 2 * 4);
+  EXPECT_EQ(fw.bytes, 512 + 16 * 2 * 2 * 8);
   EXPECT_EQ(fused_workspace(257, 2, &fw), 1);  // two token blocks: the counts still fit 256 bytes
   EXPECT_EQ(fw.partial_off, 512);
-  EXPECT_EQ(fused_workspace(256 * 65, 1, &fw), 1);  // 65 token blocks: 260 bytes of counts
+  EXPECT_EQ(fused_workspace(256 * 33, 1, &fw), 1);  // 33 token blocks: 264 bytes of counts
   EXPECT_EQ(fw.partial_off, 256 + 512);
   EXPECT_EQ(fused_workspace(INT64_MAX / 4, 256, &fw), 0);
   alignas(16) static unsigned char wsb[4096];
-  const int64_t wsn = 512 + 16 * 16;
+  const int64_t wsn = 512 + 16 * 32;
   unsigned char* gq2 = other;
   unsigned char* gk2 = other + 1024;
   EXPECT_EQ(validate_qkv_proj_norm_rope(buf, buf + 16384, nullptr, gq2, gk2, outb, wsb, wsn, 1, 1, 4, 4, 2, 128, 1e-6f,

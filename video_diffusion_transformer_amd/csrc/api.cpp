@@ -5,6 +5,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <utility>
 
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -47,6 +48,30 @@ int rope_table(int64_t T, int64_t H, int64_t W, float theta, hipStream_t stream,
   }
   g_tabs.emplace(key, dptr);
   *out = dptr;
+  return WAN_OK;
+}
+
+// --------------------------------------------------- projection tile counters
+// The persistent projection takes its tiles from a 16-byte device counter.
+// Launches on one stream run in order, so one counter per (device, stream),
+// allocated on the first call on that stream and kept until the process ends.
+using CounterKey = std::pair<int, hipStream_t>;
+std::mutex g_cnt_mu;
+std::map<CounterKey, unsigned*> g_counters;
+
+int proj_counter(hipStream_t stream, unsigned** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return WAN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_cnt_mu);
+  auto it = g_counters.find({dev, stream});
+  if (it != g_counters.end()) {
+    *out = it->second;
+    return WAN_OK;
+  }
+  unsigned* p = nullptr;
+  if (hipMalloc(&p, 16) != hipSuccess) return WAN_E_NOMEM;
+  g_counters.emplace(CounterKey{dev, stream}, p);
+  *out = p;
   return WAN_OK;
 }
 
@@ -95,8 +120,12 @@ int wan_qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, 
   wan::Sizes z;
   int rc = wan::validate_qkv_proj(x, w_qkv, bias, qkv, B, S, heads, head_dim, &z);
   if (rc != WAN_OK || z.empty) return rc;
-  if (wan::launch_qkv_proj(x, w_qkv, bias, qkv, z.rows, static_cast<int>(3 * z.D), static_cast<int>(z.D),
-                           static_cast<hipStream_t>(stream)) != hipSuccess)
+  auto st = static_cast<hipStream_t>(stream);
+  unsigned* counter = nullptr;
+  rc = proj_counter(st, &counter);
+  if (rc != WAN_OK) return rc;
+  if (wan::launch_qkv_proj(x, w_qkv, bias, qkv, z.rows, static_cast<int>(3 * z.D), static_cast<int>(z.D), counter,
+                           st) != hipSuccess)
     return WAN_E_HIP;
   return WAN_OK;
 }

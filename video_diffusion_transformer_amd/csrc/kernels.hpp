@@ -64,9 +64,11 @@ hipError_t launch_quant_v_delayed(const void* qkv, void* vt8, const float* amax_
                                   int B, int S, int heads, hipStream_t stream);
 
 // QKV projection out[M, N] = x[M, K] w[N, K]^T (+ bias), bf16; K a multiple of
-// 64, N a multiple of 4.
+// 128, N a multiple of 4. A persistent grid takes output tiles from *counter
+// (16 bytes of device memory, cleared by the launch); launches that share a
+// counter must be ordered (same stream).
 hipError_t launch_qkv_proj(const void* x, const void* w, const void* bias, void* out, int64_t M, int N, int K,
-                           hipStream_t stream);
+                           unsigned* counter, hipStream_t stream);
 
 // The projection of M = B * S tokens with the Q/K RMSNorm and 3-D RoPE in its
 // epilogue (D = heads * 128; out [M, 3D] holds normalised, rotated Q and K and

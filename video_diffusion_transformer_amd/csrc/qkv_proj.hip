@@ -27,10 +27,13 @@
 //   * epilogue through LDS: the tile is written to LDS and stored as whole
 //     256-byte row segments (8-byte stores straight from the MFMA layout touch
 //     16 rows per store and stall the texture unit's write path: +6%);
-//   * workgroups are numbered XCD-major and then in groups of 8 token tiles
-//     sweeping the feature tiles, so the ~32 workgroups an XCD runs at once
-//     share 8 x tiles and 4 W tiles in its L2 (groups of 16 or 32 token tiles
-//     measured 10% and 20% slower).
+//   * a persistent grid (one workgroup per CU slot) takes output tiles from an
+//     atomic counter in token-block order (token block, then feature tile):
+//     the ~4 token blocks in flight share their x tiles in L2 while W (157 MB
+//     at D = 5120) streams from the 256 MB last-level cache. Measured on the
+//     480p tokens (10.3 TFLOP): 8.0 ms against 9.5 ms for one workgroup per
+//     tile in an XCD-grouped order, and 9.1 ms for one workgroup per tile in
+//     this order.
 #include <mutex>
 
 #include "common.hpp"
@@ -47,7 +50,6 @@ constexpr int kPWaves = 8, kPThreads = 64 * kPWaves;
 constexpr int kPRow = kPK * 2;                 // bytes per LDS row
 constexpr int kPTile = kPM * kPRow;            // 32 KB per operand tile
 constexpr int kPStage = 2 * kPTile;            // W tile + x tile
-constexpr int kPGroup = 8;                     // token tiles per ordering group
 constexpr int kPBlk = kPTile / 1024 / kPWaves;  // 1 KB blocks (8 rows) per wave per operand tile (4)
 constexpr int kPLoads = 2 * kPBlk;             // copies per wave per step (8)
 static_assert(kPM == kPN, "one staging layout serves both operands");
@@ -59,12 +61,6 @@ constexpr int kWaitVm0 = 0x0f70;               // s_waitcnt vmcnt(0), other coun
 // of a 512-byte window (and every 8 or 16 consecutive lanes on distinct slots
 // of 128 or 256 bytes), which the gfx950 LDS serves without bank conflicts.
 __device__ __forceinline__ int p_swz(int r) { return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2); }
-
-__device__ __forceinline__ int p_xcd_remap(int bid, int nb) {
-  const int xcd = bid & 7, j = bid >> 3;
-  const int q = nb >> 3, r = nb & 7;
-  return xcd * q + (xcd < r ? xcd : r) + j;
-}
 
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -180,9 +176,17 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ x, const 
 // u ^ f(row), f(row) = 2 ((row >> 1) & 15): even, so 16-byte pieces stay whole,
 // and the writes of a half-wave (16 rows x 2 units) and the reads (2 rows x 256
 // bytes) both cover distinct banks.
+//
+// The lane index passes through an empty asm statement so that the LDS
+// addresses derived from it are computed here and not hoisted out of a
+// persistent kernel's tile loop: hoisted, 16 of them would stay live across the
+// GEMM, spill, and every store would first wait (vmcnt) for its reload -- and
+// with it for all earlier stores.
 template <class Pack>
 __device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, int M, int N, int m0, int n0,
-                                           unsigned char* __restrict__ smem, int wave, int lane, Pack pk) {
+                                           unsigned char* __restrict__ smem, int wave, int lane_in, Pack pk) {
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
   const int l16 = lane & 15, grp = lane >> 4;
   const int wn = wave & 1, wm = wave >> 1;
   unsigned char* ep = smem + wave * (64 * 256);
@@ -218,41 +222,6 @@ __device__ __forceinline__ void load_bias4(const uint16_t* __restrict__ bias, in
   }
 }
 
-__global__ void __launch_bounds__(kPThreads, 1)
-qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-                uint16_t* __restrict__ out, int M, int N, int K, int ntm, int ntn) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kPStage];
-
-  // Tile order: XCD-major, then groups of kPGroup token tiles x all feature tiles.
-  const int lid = p_xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = kPGroup * ntn;
-  const int group = lid / per_group;
-  const int first_tm = group * kPGroup;
-  const int gm = min(ntm - first_tm, kPGroup);
-  const int rr = lid - group * per_group;
-  const int tm = first_tm + rr % gm, tn = rr / gm;
-  const int m0 = tm * kPM, n0 = tn * kPN;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = lane >> 4, wn = wave & 1;
-
-  f32x4_t acc[8][4];
-  gemm_tile(x, w, M, N, K, m0, n0, smem, wave, lane, acc);
-
-  // Bias added in fp32, one rounding to bf16.
-  const int nb = n0 + 128 * wn;
-  float bv[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) load_bias4(bias, nb + 16 * i + 4 * grp, N, bv[i]);
-  store_tile(out, M, N, m0, n0, smem, wave, lane, [&](int i, int j) {
-    uint2 o;
-    o.x = pack_bf16x2(acc[i][j][0] + bv[i][0], acc[i][j][1] + bv[i][1]);
-    o.y = pack_bf16x2(acc[i][j][2] + bv[i][2], acc[i][j][3] + bv[i][3]);
-    return o;
-  });
-}
-
 // ---------------------------------------------------------------------------
 // The projection with the Q/K RMSNorm and 3-D RoPE in its epilogue (the qkv_cte
 // kernel of "Optimizing High-Quality Offline Video Generation", NKI kernels: QKV
@@ -263,23 +232,28 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
 // of one token block exchange per-token partial sums of squares: each tile
 // rounds its outputs to bf16 (the projection's own rounding point), publishes
 // every token's sum of squares over each of its 128-feature wave columns, waits
-// until all Q and K columns of its token block have published, and then
-// normalises, rotates and rounds its tile in registers. The unnormalised Q and
-// K never reach memory.
+// until all columns of its part (Q, or K) of its token block have published,
+// and then normalises, rotates and rounds its tile in registers. The
+// unnormalised Q and K never reach memory.
 //
 // Scheduling: a persistent grid (one workgroup per CU slot) takes tiles from an
-// atomic counter in token-block order (token block, then feature tile). A
-// workgroup publishes before it waits and waits only for the Q/K tiles of its
-// own token block. Waiting workgroups hold Q/K tiles of the lowest unfinished
-// token block only (every tile of a lower block has been taken and published),
-// so at most heads - 1 wait at once (some Q/K tile of that block is still
-// untaken); with room on the device for `heads` workgroups, some workgroup is
-// always free to take the missing tiles, and every wait ends. A bounded spin guards the rest (e.g. the device held by
-// other work): past the limit the workgroup sets the error word of the
-// workspace and stores NaN bits for its Q and K outputs.
+// atomic counter in token-block order (token block, then feature tile: the Q
+// tiles of a block, then its K tiles, then V). A workgroup publishes before it
+// waits and waits only for the tiles of its own (token block, part) unit.
+// Taking the units in order, waiting workgroups hold tiles of the lowest
+// unfinished unit only (every tile of a lower unit has been taken and
+// published), so fewer wait than the unit has tiles (some tile of it is still
+// untaken): at most about heads / 2. With room on the device for `heads`
+// workgroups, some workgroup is always free to take the missing tiles, and
+// every wait ends. A bounded spin guards the rest (e.g. the device held by
+// other work): past the limit the wave sets the error word of the workspace
+// and stores NaN bits for its Q and K outputs. Counting Q and K apart halves
+// the span of tiles a wait covers (measured: the wait was 7% of the kernel
+// with one count per token block).
 // ---------------------------------------------------------------------------
 constexpr int kPairsT = 22, kPairsH = 21, kPairsW = 21;  // rotary pairs per axis (44/42/42 channels)
 constexpr unsigned kSpinLimit = 1u << 20;                // polls of a token block's arrival count (about 1 s)
+constexpr unsigned kReadLimit = 1u << 16;                // re-reads of partial sums whose marker is not yet visible
 
 struct NormRopeArgs {
   const uint16_t* gq;  // RMSNorm weights of Q and of K, [D] bf16
@@ -288,28 +262,31 @@ struct NormRopeArgs {
   int S, H, W, offH, offW, heads;
   float inv_d, eps;
   unsigned* ctl;       // [0] tile counter, [1] error word (a wait hit the spin limit)
-  unsigned* arrive;    // [ntm] published Q/K wave columns per token block
-  float* partial;      // [M][2 heads] sums of squares per token and wave column (Q heads, then K heads)
+  unsigned* arrive;    // [ntm][2] published Q and K wave columns per token block
+  uint64_t* partial;   // [2 heads][M] (1 << 32 | sum-of-squares bits) per wave column (Q heads, then K heads) and token
 };
 
-__global__ void __launch_bounds__(256) zero_u32_kernel(unsigned* __restrict__ p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// Zero n 16-byte words (grid-stride).
+__global__ void __launch_bounds__(256) zero16_kernel(u32x4_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
+// Norm = false: the plain projection (bias, bf16 rounding, store); only
+// na.ctl (the tile counter) is used.
+template <bool Norm>
 __global__ void __launch_bounds__(kPThreads, 1)
-qkv_proj_norm_rope_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N, int K, int ntm,
-                          int ntn, NormRopeArgs na) {
+qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+                uint16_t* __restrict__ out, int M, int N, int K, int ntm, int ntn, NormRopeArgs na) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kPStage];
-  __shared__ int tile_sh, late_sh;
+  __shared__ int tile_sh, late_sh;  // the tile taken; its arrival wait timed out
+  __shared__ float xsum[kPWaves][64];  // sums of squares passed between the two waves of a row
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
   const int wn = wave & 1, wm = wave >> 1;
   const int D = na.heads * 128;
-  const int slots = 2 * na.heads;  // Q and K wave columns of a token block
   const int ntiles = ntm * ntn;
 
   for (;;) {
@@ -337,13 +314,32 @@ qkv_proj_norm_rope_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
         for (int e = 0; e < 4; ++e) acc[i][j][e] = static_cast<float>(static_cast<__bf16>(acc[i][j][e] + bv[e]));
     }
 
-    // Q/K wave columns in this tile (0, 1 or 2); whether this wave holds one.
-    const int qk_cols = (n0 < N && n0 / D < 2 ? 1 : 0) + (n0 + 128 < N && (n0 + 128) / D < 2 ? 1 : 0);
-    const bool qk = nb < N && part < 2;
+    // The tile's Q and its K wave columns (0, 1 or 2 of each); whether this wave holds one.
+    int cols_q = 0, cols_k = 0;
+    if (Norm) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int f = n0 + 128 * h;
+        cols_q += f < N && f / D == 0;
+        cols_k += f < N && f / D == 1;
+      }
+    }
+    const int qk_cols = cols_q + cols_k;
+    const bool qk = Norm && nb < N && part < 2;
+    // Publish, then wait. The partial sums travel as 64-bit words (value bits,
+    // 1 above them) written and read with device-scope atomic accesses: a
+    // reader that finds the marker has the value of the same word, so the
+    // exchange needs no device-wide fence (those write back and invalidate the
+    // XCD's L2, which the GEMM operands live in). The arrival count only tells
+    // the workgroup when to start reading; a word not yet visible is re-read.
+    // Layout [column][token]: one wave's 64 tokens of a column are 512
+    // contiguous bytes, read by one load instruction.
+    bool bad = false;  // this wave's wait timed out: its Q/K outputs are stored as NaN bits
+    float ssum = 0.f;  // reader: sum of squares over all Q (or K) channels of token m0 + 64 wm + lane
     if (qk_cols > 0) {
       if (qk) {
         // Sum of squares of each of the wave's 64 tokens over its 128 features.
-        const int slot = part * na.heads + (nb - part * D) / 128;
+        const int col = part * na.heads + (nb - part * D) / 128;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float ss = 0.f;
@@ -354,50 +350,79 @@ qkv_proj_norm_rope_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
           ss += __shfl_xor(ss, 16, 64);
           ss += __shfl_xor(ss, 32, 64);
           const int m = m0 + 64 * wm + 16 * j + l16;
-          if (grp == 0 && m < M) na.partial[(int64_t)m * slots + slot] = ss;
+          if (grp == 0 && m < M)
+            __hip_atomic_store(na.partial + (int64_t)col * M + m, (uint64_t(1) << 32) | __float_as_uint(ss),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __threadfence();  // release: the partial sums are visible device-wide before the arrival below
+        // The stores have completed before the arrival below is counted, so a
+        // reader that sees the count complete finds the words (re-reads stay rare).
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
       }
       __syncthreads();
       if (tid == 0) {
-        atomicAdd(na.arrive + tm, static_cast<unsigned>(qk_cols));
-        unsigned spins = 0;
+        // Q and K of a token block are counted apart: a tile waits only for
+        // the columns of the part(s) it holds.
         int late = 0;
-        while (__hip_atomic_load(na.arrive + tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               static_cast<unsigned>(slots)) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > kSpinLimit) {
-            atomicOr(na.ctl + 1, 1u);
-            late = 1;
-            break;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int cols = p == 0 ? cols_q : cols_k;
+          if (cols == 0) continue;
+          unsigned* cnt = na.arrive + 2 * tm + p;
+          atomicAdd(cnt, static_cast<unsigned>(cols));
+          unsigned spins = 0;
+          while (!late && __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                              static_cast<unsigned>(na.heads)) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > kSpinLimit) late = 1;
           }
         }
-        __threadfence();  // acquire: the other columns' partial sums are read after this point
         late_sh = late;
       }
       __syncthreads();
+      bad = qk && late_sh != 0;
+
+      // Both wave columns of the tile in Q (or both in K): the two waves of a
+      // row read alternate columns and add each other's sums (through LDS).
+      const bool split = qk_cols == 2 && n0 / D == (n0 + 128) / D;
+      if (qk) {
+        const int mrow = min(m0 + 64 * wm + lane, M - 1);  // rows past M: any row of the block (not stored)
+        const uint64_t* pr = na.partial + (int64_t)(part * na.heads) * M + mrow;
+        const int c0 = split ? wn : 0, cstep = split ? 2 : 1;
+        for (unsigned tries = 0; !bad; ++tries) {
+          bool ready = true;
+          float sc = 0.f;
+          for (int c = c0; c < na.heads; c += cstep) {
+            const uint64_t v = __hip_atomic_load(pr + (int64_t)c * M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ready = ready && (v >> 32) != 0;
+            sc += __uint_as_float(static_cast<uint32_t>(v));
+          }
+          ssum = sc;
+          if (__all(ready)) break;
+          if (tries > kReadLimit) bad = true;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (bad && lane == 0) atomicOr(na.ctl + 1, 1u);
+      }
+      if (split) {
+        xsum[wave][lane] = ssum;
+        __syncthreads();
+        ssum += xsum[wave ^ 1][lane];  // same sum in both waves: fp32 addition commutes
+      }
     }
 
-    // A timed-out wait leaves the norm unknown: its Q/K outputs are stored as NaN bits.
-    const bool bad = qk && qk_cols > 0 && late_sh != 0;
     if (qk) {
       const uint16_t* g = part == 0 ? na.gq : na.gk;
       const int cbase = nb - part * D;  // channel of this wave's first feature within Q or K
       float r[4];                       // (mean square + eps)^-1/2 of the wave's tokens 16 j + l16
-      int f_[4], y_[4], x_[4];          // their (frame, row, column) on the token grid
+      int tb[4][3];                     // their rotary table rows (frame, row, column axis), minus the axis' first pair
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int m = min(m0 + 64 * wm + 16 * j + l16, M - 1);  // rows past M: any valid row (not stored)
-        const float* pr = na.partial + (int64_t)m * slots + part * na.heads;
-        float ss = 0.f;
-        for (int c = grp; c < na.heads; c += 4) ss += pr[c];
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
+        const float ss = __shfl(ssum, 16 * j + l16, 64);
         r[j] = rsqrtf(ss * na.inv_d + na.eps);
-        const int s = m % na.S;
-        f_[j] = s / (na.H * na.W);
-        y_[j] = (s / na.W) % na.H;
-        x_[j] = s % na.W;
+        const int s = min(m0 + 64 * wm + 16 * j + l16, M - 1) % na.S;
+        tb[j][0] = (s / (na.H * na.W)) * kPairsT;
+        tb[j][1] = na.offH + ((s / na.W) % na.H) * kPairsH - kPairsT;
+        tb[j][2] = na.offW + (s % na.W) * kPairsW - (kPairsT + kPairsH);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -406,13 +431,12 @@ qkv_proj_norm_rope_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
         const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
         const int p0 = (c & 127) >> 1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int h = 0; h < 2; ++h) {
+          const int p = p0 + h;
+          const int ax = p < kPairsT ? 0 : (p < kPairsT + kPairsH ? 1 : 2);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int p = p0 + h;
-            const float2 cs = p < kPairsT ? na.tab[f_[j] * kPairsT + p]
-                                          : (p < kPairsT + kPairsH ? na.tab[na.offH + y_[j] * kPairsH + (p - kPairsT)]
-                                                                   : na.tab[na.offW + x_[j] * kPairsW + (p - kPairsT - kPairsH)]);
+          for (int j = 0; j < 4; ++j) {
+            const float2 cs = na.tab[p + (ax == 0 ? tb[j][0] : (ax == 1 ? tb[j][1] : tb[j][2]))];
             // norm, x gamma, bf16 rounding point; rotation in fp32 (bf16 at the store)
             const uint32_t nv = pack_bf16x2(acc[i][j][2 * h] * r[j] * gv[2 * h], acc[i][j][2 * h + 1] * r[j] * gv[2 * h + 1]);
             const float a = bf16_lo(nv), b = bf16_hi(nv);
@@ -432,59 +456,79 @@ qkv_proj_norm_rope_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
   }
 }
 
-}  // namespace
-
-hipError_t launch_qkv_proj(const void* x, const void* w, const void* bias, void* out, int64_t M, int N, int K,
-                           hipStream_t stream) {
-  const int64_t ntm = (M + kPM - 1) / kPM;
-  const int ntn = (N + kPN - 1) / kPN;
-  const int64_t nblocks = ntm * ntn;
-  if (nblocks > INT32_MAX || ntm > INT32_MAX / kPGroup / ntn) return hipErrorInvalidConfiguration;
-  // A buffer descriptor covers one operand tile: 256 rows of K bf16 must stay
-  // within its 32-bit byte range.
-  if ((int64_t)kPM * K * 2 > (int64_t)INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qkv_proj_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kPThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
-                     static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), static_cast<int>(M), N, K,
-                     static_cast<int>(ntm), ntn);
-  return hipGetLastError();
-}
-
-}  // namespace wan
-
-namespace wan {
-
-// Workgroups of the fused kernel the device holds at once (cached per device).
-static int fused_capacity(int dev) {
+// Workgroups of the persistent kernel the device holds at once (cached per device).
+static int proj_capacity(int dev) {
   static std::mutex mu;
   static int cap[64] = {};
   if (dev < 0 || dev >= 64) return 0;
   std::lock_guard<std::mutex> lock(mu);
   if (!cap[dev]) {
-    int cus = 0, per_cu = 0;
+    int cus = 0, per_cu = 0, per_cu_norm = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, qkv_proj_norm_rope_kernel, kPThreads, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, qkv_proj_kernel<false>, kPThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_norm, qkv_proj_kernel<true>, kPThreads, 0) !=
+            hipSuccess)
       return 0;
-    cap[dev] = cus * per_cu;
+    cap[dev] = cus * (per_cu < per_cu_norm ? per_cu : per_cu_norm);
   }
   return cap[dev];
+}
+
+// Tile counts of M x N; false if they (or an operand tile's byte range, which a
+// buffer descriptor addresses with 32 bits) do not fit the kernel's int32 math.
+static bool proj_tiles(int64_t M, int N, int K, int64_t* ntm, int* ntn) {
+  *ntm = (M + kPM - 1) / kPM;
+  *ntn = (N + kPN - 1) / kPN;
+  return *ntm <= INT32_MAX / 2 / *ntn && (int64_t)kPM * K * 2 <= (int64_t)INT32_MAX;
+}
+
+static hipError_t clear_words(void* p, int64_t bytes, hipStream_t stream) {
+  const int64_t nz = bytes / 16;
+  const int64_t blocks = (nz + 255) / 256;
+  hipLaunchKernelGGL(zero16_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
+                     static_cast<u32x4_t*>(p), nz);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qkv_proj(const void* x, const void* w, const void* bias, void* out, int64_t M, int N, int K,
+                           unsigned* counter, hipStream_t stream) {
+  int64_t ntm;
+  int ntn;
+  if (!proj_tiles(M, N, K, &ntm, &ntn)) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int cap = proj_capacity(dev);
+  if (cap < 1) return hipErrorInvalidConfiguration;
+  const int ntiles = static_cast<int>(ntm * ntn);
+  NormRopeArgs na = {};
+  na.heads = K / 128;
+  na.ctl = counter;
+  e = clear_words(counter, 16, stream);  // the tile counter starts at zero
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qkv_proj_kernel<false>, dim3(cap < ntiles ? cap : ntiles), dim3(kPThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                     static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), static_cast<int>(M), N, K,
+                     static_cast<int>(ntm), ntn, na);
+  return hipGetLastError();
 }
 
 hipError_t launch_qkv_proj_norm_rope(const void* x, const void* w, const void* bias, const void* gq, const void* gk,
                                      const float2* tab, void* out, void* workspace, int64_t M, int heads, int S, int T,
                                      int H, int W, float eps, hipStream_t stream) {
   const int D = heads * 128, N = 3 * D, K = D;
-  const int64_t ntm = (M + kPM - 1) / kPM;
-  const int ntn = (N + kPN - 1) / kPN;
-  if (ntm * ntn > INT32_MAX / 2 || (int64_t)kPM * K * 2 > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  int64_t ntm;
+  int ntn;
+  if (!proj_tiles(M, N, K, &ntm, &ntn)) return hipErrorInvalidValue;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const int cap = fused_capacity(dev);
+  const int cap = proj_capacity(dev);
   // At most heads - 1 workgroups wait at once; one more must fit for every wait to end.
   if (cap < heads) return hipErrorInvalidConfiguration;
   const int ntiles = static_cast<int>(ntm * ntn);
-  const int grid = cap < ntiles ? cap : ntiles;
   FusedWorkspace fw;
   if (!fused_workspace(M, heads, &fw)) return hipErrorInvalidValue;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -502,14 +546,13 @@ hipError_t launch_qkv_proj_norm_rope(const void* x, const void* w, const void* b
   na.eps = eps;
   na.ctl = reinterpret_cast<unsigned*>(ws);
   na.arrive = reinterpret_cast<unsigned*>(ws + fw.arrive_off);
-  na.partial = reinterpret_cast<float*>(ws + fw.partial_off);
-  // Counters and error word start at zero: a fill kernel (no memset node if the call is captured in a graph).
-  const int64_t nz = 64 + ntm;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(static_cast<unsigned>((nz + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<unsigned*>(ws), nz);
-  e = hipGetLastError();
+  na.partial = reinterpret_cast<uint64_t*>(ws + fw.partial_off);
+  // Counters, error word and the markers of the partial sums start at zero: a
+  // fill kernel over the whole workspace (no memset node if the call is
+  // captured in a graph).
+  e = clear_words(ws, fw.bytes, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(qkv_proj_norm_rope_kernel, dim3(grid), dim3(kPThreads), 0, stream,
+  hipLaunchKernelGGL(qkv_proj_kernel<true>, dim3(cap < ntiles ? cap : ntiles), dim3(kPThreads), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
                      static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), static_cast<int>(M), N, K,
                      static_cast<int>(ntm), ntn, na);

@@ -216,9 +216,10 @@ inline int validate_qkv_proj(const void* x, const void* w, const void* bias, con
 }
 
 // Workspace of the projection with the norm + RoPE epilogue, for `rows` tokens
-// and `heads` heads: 256 bytes of control words (tile counter, error word), one
-// 32-bit arrival count per 256-token block (the span rounded up to 256 bytes),
-// then rows x 2 heads fp32 partial sums of squares. False on overflow.
+// and `heads` heads: 256 bytes of control words (tile counter, error word), two
+// 32-bit arrival counts (Q, K) per 256-token block (the span rounded up to 256 bytes),
+// then rows x 2 heads 64-bit words (a partial sum of squares and its marker).
+// False on overflow.
 struct FusedWorkspace {
   int64_t arrive_off, partial_off, bytes;
 };
@@ -227,9 +228,9 @@ inline bool fused_workspace(int64_t rows, int64_t heads, FusedWorkspace* f) {
   if (rows < 0 || heads < 1 || rows > INT64_MAX / 4 - kFusedTileTokens) return false;
   const int64_t ntm = (rows + kFusedTileTokens - 1) / kFusedTileTokens;
   int64_t part;
-  if (!mul_ok(rows, 8 * heads, &part)) return false;
+  if (!mul_ok(rows, 16 * heads, &part)) return false;
   f->arrive_off = 256;
-  f->partial_off = 256 + (4 * ntm + 255) / 256 * 256;
+  f->partial_off = 256 + (8 * ntm + 255) / 256 * 256;
   if (part > INT64_MAX - f->partial_off) return false;
   f->bytes = f->partial_off + part;
   return true;
