@@ -38,7 +38,9 @@ timed steps. One JSON line is printed.
   qkv_proj    (bf16 workloads) the QKV projection x W^T + b that produces the
               packed [Q|K|V] buffer the step reads: FLOP per launch over the
               launch time from HIP events on its stream, against the bf16
-              MFMA peak; not part of the step or of value.
+              MFMA peak; with_norm_rope: the projection with the norm + RoPE
+              fused into its epilogue against the two calls; not part of the
+              step or of value.
 """
 
 import argparse
@@ -55,7 +57,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "attn_fwd_fp8": "attn_fwd_fp8.hip",
-                  "qknorm_rope": "qknorm_rope.hip", "qkv_proj": "qkv_proj.hip"}
+                  "qknorm_rope": "qknorm_rope.hip", "qkv_proj": "qkv_proj.hip", "qkv_proj_norm_rope": "qkv_proj.hip"}
 EXTRA_WORKLOADS = ("720p", "720p_fp8", "long")
 
 
@@ -180,7 +182,8 @@ def ring_share(w, qkv, cp, reps=3):
             wan_attn.attn_merge(acc, acc_lse, o, lse, w.heads, out_bf16=out16 if c == cp - 1 else None)
 
     def timed(fn):
-        fn()
+        for _ in range(2):
+            fn()
         torch.cuda.synchronize()
         t0, t1 = E(), E()
         t0.record(stream)
@@ -201,8 +204,9 @@ def ring_share(w, qkv, cp, reps=3):
 
 def qkv_proj(w, dev, reps=3):
     """The QKV projection on the workload's token matrix: x [B, S, D] times the
-    fused weight [3D, D] plus bias into the packed [B, S, 3D] buffer. One
-    warm-up call, then reps calls timed with HIP events on the stream."""
+    fused weight [3D, D] plus bias into the packed [B, S, 3D] buffer. Two
+    warm-up calls, then reps calls timed with HIP events on the stream (the
+    same for the projection + norm + RoPE, fused and as two calls)."""
     import torch
 
     from video_diffusion_transformer_amd import synth, wan_attn
@@ -211,23 +215,47 @@ def qkv_proj(w, dev, reps=3):
         return None
     x = synth.make_tokens(w.B, w.S, w.D, seed=w.seed, device=dev)
     wq, bq = synth.make_qkv_weights(w.D, seed=w.seed, device=dev)
+    gq, gk = synth.make_gammas(w.D, seed=w.seed, device=dev)
+    grid = (w.T, w.H, w.W)
     out = torch.empty((w.B, w.S, 3 * w.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(wan_attn.qkv_proj_norm_rope_workspace_bytes(w.B, w.S, w.heads), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    wan_attn.qkv_proj(x, wq, w.heads, bias=bq, out=out)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(reps):
+
+    def proj():
         wan_attn.qkv_proj(x, wq, w.heads, bias=bq, out=out)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / reps
+
+    def two_call():
+        wan_attn.qkv_proj(x, wq, w.heads, bias=bq, out=out)
+        wan_attn.qknorm_rope(out, gq, gk, grid, w.heads)
+
+    def fused():
+        wan_attn.qkv_proj_norm_rope(x, wq, gq, gk, grid, w.heads, bias=bq, out=out, workspace=ws)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    ms = timed(proj)
+    ms_two, ms_fused = timed(two_call), timed(fused)
+    if wan_attn.proj_norm_rope_error_word(ws) != 0:
+        raise RuntimeError("wan_qkv_proj_norm_rope: a token block's wait hit its spin limit")
     flop = 2.0 * w.B * w.S * 3 * w.D * w.D
     tf = flop / (ms * 1e-3) / 1e12
-    del x, wq, bq, out
+    del x, wq, bq, out, ws
     return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
             "frac": round(tf / PEAK_TFLOPS["bf16"], 4), "ms_per_launch": round(ms, 4), "flop_per_launch": flop,
-            "traffic": committed_traffic("qkv_proj", w.name)}
+            "traffic": committed_traffic("qkv_proj", w.name),
+            "with_norm_rope": {"ms_fused": round(ms_fused, 4), "ms_two_call": round(ms_two, 4),
+                               "traffic_fused": committed_traffic("qkv_proj_norm_rope", w.name),
+                               "note": "projection followed by the Q/K norm + RoPE: one fused kernel "
+                                       "(wan_qkv_proj_norm_rope) against wan_qkv_proj then wan_qknorm_rope"}}
 
 
 def skip_softmax(w, dev, threshold, reps=3):
@@ -392,7 +420,7 @@ def main():
     ap.add_argument("--ring-cp", type=int, default=8, metavar="CP",
                     help="also time one GPU's share of ring attention with the sequence split over CP ranks "
                          "(bf16 workloads; 0 to skip)")
-    ap.add_argument("--proj-reps", type=int, default=3, metavar="N",
+    ap.add_argument("--proj-reps", type=int, default=10, metavar="N",
                     help="timed calls of the QKV projection on the workload's tokens (bf16 workloads; 0 to skip)")
     ap.add_argument("--skip-threshold", type=float, default=0.02, metavar="T",
                     help="also time Skip-Softmax attention at this threshold against dense attention on a "

@@ -55,8 +55,10 @@ def _check(x, w, b, gq, gk, grid, heads, what, bias=True):
 
 
 @pytest.mark.parametrize("B,grid,heads", [(1, (1, 1, 1), 1), (1, (2, 8, 8), 2), (2, (3, 5, 7), 3),
-                                          (1, (2, 9, 15), 5), (2, (3, 10, 20), 40)])
+                                          (1, (2, 9, 15), 5), (2, (3, 10, 20), 40), (1, (1, 2, 190), 2)])
 def test_small_every_token(B, grid, heads):
+    """Every token against the oracle; the last grid is one long row (a
+    rotary table of 4,054 entries, most on the column axis)."""
     x, w, b, gq, gk = _inputs(B, grid, heads, seed=sum(grid) + heads)
     _check(x, w, b, gq, gk, grid, heads, f"B{B} {grid} h{heads}")
 
