@@ -62,9 +62,16 @@ EXTRA_WORKLOADS = ("720p", "720p_fp8", "long")
 
 
 def kernel_source_hash(name):
-    path = os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc", KERNEL_SOURCES[name])
+    """Hash of a kernel's source file and of the per-source compiler flags it
+    is built with (a change of either invalidates its committed counters)."""
+    from video_diffusion_transformer_amd import build
+
+    src = KERNEL_SOURCES[name]
+    path = os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc", src)
     with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        h = hashlib.sha256(f.read())
+    h.update(" ".join(build.kernel_flags(src)).encode())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic(kernel, workload):

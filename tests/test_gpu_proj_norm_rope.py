@@ -63,6 +63,14 @@ def test_small_every_token(B, grid, heads):
     _check(x, w, b, gq, gk, grid, heads, f"B{B} {grid} h{heads}")
 
 
+def test_wide_model():
+    """64 heads (D = 8192: a Q unit of 32 tiles, 128 K steps) on a few tokens:
+    every output against the oracle."""
+    grid, heads = (1, 1, 5), 64
+    x, w, b, gq, gk = _inputs(1, grid, heads, seed=64)
+    _check(x, w, b, gq, gk, grid, heads, "64 heads")
+
+
 def test_without_bias_and_repeat_calls():
     """No bias; two calls in a row on one workspace (its counters are cleared
     by each call) give the same bits; a call on a smaller input after a larger

@@ -39,12 +39,24 @@ def common_flags():
             "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source scheduler choice. The attention kernels are built with LLVM's
+# max-ILP machine scheduler: same instructions (bit-identical outputs), ordered
+# for instruction-level parallelism instead of register pressure -- measured
+# +4% on the bf16 kernel (480p: 33.55 -> 32.26 ms on one box, interleaved
+# calls) and +0.4% on the fp8 kernel; the projection and norm kernels measured
+# no gain and keep the default scheduler.
+SCHED_FLAGS = {
+    "attn_fwd.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+    "attn_fwd_fp8.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def kernel_flags(src):
     """Kernel sources may assume no NaN arithmetic (max/min then need no NaN
     canonicalisation; NaN inputs give unspecified results). The host-side
     entry points (api.cpp) are built without that assumption, so their checks
-    of scalar arguments still see a NaN."""
-    return [] if src.endswith(".cpp") else ["-fno-honor-nans"]
+    of scalar arguments still see a NaN. Plus the source's scheduler flags."""
+    return [] if src.endswith(".cpp") else ["-fno-honor-nans", *SCHED_FLAGS.get(src, [])]
 
 
 def _compile(src):
