@@ -56,21 +56,27 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
-KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "attn_fwd_fp8": "attn_fwd_fp8.hip",
-                  "qknorm_rope": "qknorm_rope.hip", "qkv_proj": "qkv_proj.hip", "qkv_proj_norm_rope": "qkv_proj.hip"}
+# The files each measured kernel is built from (its launch source first).
+KERNEL_SOURCES = {"attn_fwd": ("attn_fwd.hip", "attn_fwd_impl.hpp", "common.hpp"),
+                  "attn_fwd_fp8": ("attn_fwd_fp8.hip", "common.hpp"),
+                  "qknorm_rope": ("qknorm_rope.hip", "common.hpp"),
+                  "qkv_proj": ("qkv_proj.hip", "common.hpp"),
+                  "qkv_proj_norm_rope": ("qkv_proj.hip", "common.hpp")}
 EXTRA_WORKLOADS = ("720p", "720p_fp8", "long")
 
 
 def kernel_source_hash(name):
-    """Hash of a kernel's source file and of the per-source compiler flags it
-    is built with (a change of either invalidates its committed counters)."""
+    """Hash of a kernel's source files and of the compiler flags its launch
+    source is built with (a change of either invalidates its committed
+    counters)."""
     from video_diffusion_transformer_amd import build
 
-    src = KERNEL_SOURCES[name]
-    path = os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc", src)
-    with open(path, "rb") as f:
-        h = hashlib.sha256(f.read())
-    h.update(" ".join(build.kernel_flags(src)).encode())
+    files = KERNEL_SOURCES[name]
+    h = hashlib.sha256()
+    for src in files:
+        with open(os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(build.kernel_flags(files[0])).encode())
     return h.hexdigest()[:16]
 
 

@@ -21,8 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwan_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "noalloc.hip", "qkv_proj.hip", "qknorm_rope.hip", "attn_fwd.hip", "attn_merge.hip",
-           "quant_fp8.hip", "attn_fwd_fp8.hip"]
+SOURCES = ["api.cpp", "noalloc.hip", "qkv_proj.hip", "qknorm_rope.hip", "attn_fwd.hip", "attn_fwd_exact.hip",
+           "attn_merge.hip", "quant_fp8.hip", "attn_fwd_fp8.hip"]
 
 
 def hipcc():
@@ -42,9 +42,10 @@ def common_flags():
 # Per-source scheduler choice. The attention kernels are built with LLVM's
 # max-ILP machine scheduler: same instructions (bit-identical outputs), ordered
 # for instruction-level parallelism instead of register pressure -- measured
-# +4% on the bf16 kernel (480p: 33.55 -> 32.26 ms on one box, interleaved
-# calls) and +0.4% on the fp8 kernel; the projection and norm kernels measured
-# no gain and keep the default scheduler.
+# +4% on the bf16 step kernel (480p: 33.55 -> 32.26 ms on one box, interleaved
+# calls), +3% on Skip-Softmax and +0.4% on the fp8 kernel. The bf16 instances
+# that return a log-sum-exp (attn_fwd_exact.hip) measured 1.5-4% slower with
+# it, and the projection and norm kernels no gain: they keep the default.
 SCHED_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
     "attn_fwd_fp8.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],

@@ -30,6 +30,9 @@ hipError_t launch_rope_table(float2* tab, int T, int H, int W, float theta, hipS
 // bf16 attention forward over the packed buffer.
 hipError_t launch_attn_fwd(const void* qkv, void* out, float* lse, int B, int S, int heads,
                            float softmax_scale, hipStream_t stream);
+// The instance of launch_attn_fwd that also writes the log-sum-exp (lse != NULL).
+hipError_t launch_attn_fwd_lse(const void* qkv, void* out, float* lse, int B, int S, int heads, float softmax_scale,
+                               hipStream_t stream);
 
 // Skip-Softmax (threshold mode) variant of it; kept (optional) receives the
 // per-(query block, key tile) decisions.
