@@ -30,10 +30,10 @@
 //   * a persistent grid (one workgroup per CU slot) takes output tiles from an
 //     atomic counter in token-block order (token block, then feature tile):
 //     the ~4 token blocks in flight share their x tiles in L2 while W (157 MB
-//     at D = 5120) streams from the 256 MB last-level cache. Measured on the
-//     480p tokens (10.3 TFLOP): 8.0 ms against 9.5 ms for one workgroup per
-//     tile in an XCD-grouped order, and 9.1 ms for one workgroup per tile in
-//     this order.
+//     at D = 5120) streams from the 256 MB last-level cache. Measured against
+//     one workgroup per tile in an XCD-grouped order (interleaved calls):
+//     480p (10.3 TFLOP) 7.90 against 7.80 ms, 720p (23.8 TFLOP) 18.2 against
+//     18.9 ms; the fused norm + RoPE epilogue below needs the persistent grid.
 #include <mutex>
 
 #include "common.hpp"
@@ -248,8 +248,8 @@ __device__ __forceinline__ void load_bias4(const uint16_t* __restrict__ bias, in
 // every wait ends. A bounded spin guards the rest (e.g. the device held by
 // other work): past the limit the wave sets the error word of the workspace
 // and stores NaN bits for its Q and K outputs. Counting Q and K apart halves
-// the span of tiles a wait covers (measured: the wait was 7% of the kernel
-// with one count per token block).
+// the span of tiles a wait covers (with one count per token block, publishing
+// and waiting took 6.9% of the kernel at 480p; counted apart, 0.05 ms less).
 // ---------------------------------------------------------------------------
 constexpr int kPairsT = 22, kPairsH = 21, kPairsW = 21;  // rotary pairs per axis (44/42/42 channels)
 constexpr unsigned kSpinLimit = 1u << 20;                // polls of a token block's arrival count (about 1 s)
