@@ -3,9 +3,10 @@
 Both take their output tiles from a device counter that each launch clears
 with a fill kernel (no memset node), so a graph replays them correctly: every
 replay, with eager work and synchronisations between the replays, must give
-the eager result bit for bit (wan_qkv_proj, and wan_qkv_proj_norm_rope with
-its caller-owned workspace). Tables and the per-stream counter are made by a
-first call on the capture stream before the capture starts.
+the eager result bit for bit (wan_qkv_proj, whose captured call keeps the
+counter slot it took at capture time, and wan_qkv_proj_norm_rope with its
+caller-owned workspace). The rotary tables and the counter ring are made by a
+first call before the capture starts.
 """
 
 import pytest
@@ -45,7 +46,7 @@ def test_graph_replays_equal_eager(fused):
 
     s.wait_stream(torch.cuda.current_stream(DEV))
     with torch.cuda.stream(s):
-        call()                       # tables and the stream's tile counter exist before the capture
+        call()                       # the tables and the counter ring exist before the capture
     s.synchronize()
     eager = out.clone()
     if fused:

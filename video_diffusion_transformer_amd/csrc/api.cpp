@@ -52,26 +52,29 @@ int rope_table(int64_t T, int64_t H, int64_t W, float theta, hipStream_t stream,
 }
 
 // --------------------------------------------------- projection tile counters
-// The persistent projection takes its tiles from a 16-byte device counter.
-// Launches on one stream run in order, so one counter per (device, stream),
-// allocated on the first call on that stream and kept until the process ends.
-using CounterKey = std::pair<int, hipStream_t>;
+// The persistent projection takes its tiles from a 16-byte device counter that
+// the launch clears first. Each call takes the next slot of a ring of 65,536
+// counters per device (1 MB, allocated on the first call on the device and
+// kept until the process ends), so calls on different streams, or on a stream
+// handle reused after a destroy, never share a counter unless 65,536 calls
+// are in flight at once.
+constexpr int kCounterSlots = 1 << 16;
+constexpr int kMaxDevices = 64;
 std::mutex g_cnt_mu;
-std::map<CounterKey, unsigned*> g_counters;
+unsigned char* g_counter_ring[kMaxDevices] = {};
+uint32_t g_counter_next[kMaxDevices] = {};
 
-int proj_counter(hipStream_t stream, unsigned** out) {
+int proj_counter(unsigned** out) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return WAN_E_HIP;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WAN_E_HIP;
   std::lock_guard<std::mutex> lock(g_cnt_mu);
-  auto it = g_counters.find({dev, stream});
-  if (it != g_counters.end()) {
-    *out = it->second;
-    return WAN_OK;
+  if (!g_counter_ring[dev]) {
+    void* p = nullptr;
+    if (hipMalloc(&p, static_cast<size_t>(kCounterSlots) * 16) != hipSuccess) return WAN_E_NOMEM;
+    g_counter_ring[dev] = static_cast<unsigned char*>(p);
   }
-  unsigned* p = nullptr;
-  if (hipMalloc(&p, 16) != hipSuccess) return WAN_E_NOMEM;
-  g_counters.emplace(CounterKey{dev, stream}, p);
-  *out = p;
+  const uint32_t slot = g_counter_next[dev]++ % kCounterSlots;
+  *out = reinterpret_cast<unsigned*>(g_counter_ring[dev] + static_cast<size_t>(slot) * 16);
   return WAN_OK;
 }
 
@@ -122,7 +125,7 @@ int wan_qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, 
   if (rc != WAN_OK || z.empty) return rc;
   auto st = static_cast<hipStream_t>(stream);
   unsigned* counter = nullptr;
-  rc = proj_counter(st, &counter);
+  rc = proj_counter(&counter);
   if (rc != WAN_OK) return rc;
   if (wan::launch_qkv_proj(x, w_qkv, bias, qkv, z.rows, static_cast<int>(3 * z.D), static_cast<int>(z.D), counter,
                            st) != hipSuccess)

@@ -69,7 +69,7 @@ hipError_t launch_quant_v_delayed(const void* qkv, void* vt8, const float* amax_
 // QKV projection out[M, N] = x[M, K] w[N, K]^T (+ bias), bf16; K a multiple of
 // 128, N a multiple of 4. A persistent grid takes output tiles from *counter
 // (16 bytes of device memory, cleared by the launch); launches that share a
-// counter must be ordered (same stream).
+// counter must not overlap.
 hipError_t launch_qkv_proj(const void* x, const void* w, const void* bias, void* out, int64_t M, int N, int K,
                            unsigned* counter, hipStream_t stream);
 
