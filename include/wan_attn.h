@@ -195,7 +195,10 @@ int wan_qknorm_rope(void *qkv, const void *gamma_q, const void *gamma_k,
  *              token block's wait for its partial sums hit the kernel's spin
  *              limit (about a second: only when other work holds the device);
  *              the Q and K outputs of such blocks are then NaN. Calls that
- *              share a workspace must be ordered (same stream).
+ *              share a workspace must be ordered (same stream). The
+ *              environment variable WAN_PROJ_NORM_SPIN_LIMIT, read at each
+ *              call, lowers the wait bound (polls; tests force the time-out
+ *              path with 0).
  * Launch: a persistent grid, one workgroup per CU slot, taking output tiles
  * from a counter in the workspace; requires room on the device for `heads`
  * workgroups at once (WAN_E_UNSUPPORTED otherwise).

@@ -123,6 +123,38 @@ def test_full_480p_every_token():
     print(f"480p fused projection + norm + RoPE: exact {res['exact']:.6f}, max err {res['max']:.3g}")
 
 
+def test_forced_wait_timeouts(monkeypatch):
+    """The bounded waits' time-out path, forced from the host: with
+    WAN_PROJ_NORM_SPIN_LIMIT=0 a wave whose (token block, part) unit is not
+    complete at its first poll gives up (every wait still ends). V stays
+    exact; every Q/K output is either the normal result's bits or NaN; NaNs
+    appear exactly when the workspace's error word is set. 16 token blocks x
+    60 tiles on a 256-workgroup grid: the tiles of later units are taken over
+    time, so some wave finds its unit incomplete."""
+    grid, heads = (4, 16, 32), 40
+    x, w, b, gq, gk = _inputs(2, grid, heads, seed=31)
+    ref, ws = wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, bias=b)
+    torch.cuda.synchronize()
+    assert wan_attn.proj_norm_rope_error_word(ws) == 0
+    monkeypatch.setenv("WAN_PROJ_NORM_SPIN_LIMIT", "0")
+    out, ws2 = wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, bias=b)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("WAN_PROJ_NORM_SPIN_LIMIT")
+    D = heads * 128
+    assert torch.equal(out[..., 2 * D:], ref[..., 2 * D:])
+    qk, rq = out[..., :2 * D], ref[..., :2 * D]
+    nan = torch.isnan(qk.float())
+    assert torch.equal(qk[~nan], rq[~nan])
+    err = wan_attn.proj_norm_rope_error_word(ws2)
+    assert (err != 0) == bool(nan.any())
+    assert bool(nan.any()), "no wave timed out"
+    print(f"forced time-outs: {nan.float().mean().item():.3f} of the Q/K outputs are NaN")
+    # and the normal bounds again: no time-out
+    out3, ws3 = wan_attn.qkv_proj_norm_rope(x, w, gq, gk, grid, heads, bias=b)
+    torch.cuda.synchronize()
+    assert wan_attn.proj_norm_rope_error_word(ws3) == 0 and torch.equal(out3, ref)
+
+
 def test_errors_and_empty():
     grid, heads = (1, 2, 4), 2
     x, w, b, gq, gk = _inputs(1, grid, heads, seed=3)

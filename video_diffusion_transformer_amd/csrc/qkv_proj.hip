@@ -34,6 +34,7 @@
 //     one workgroup per tile in an XCD-grouped order (interleaved calls):
 //     480p (10.3 TFLOP) 7.90 against 7.80 ms, 720p (23.8 TFLOP) 18.2 against
 //     18.9 ms; the fused norm + RoPE epilogue below needs the persistent grid.
+#include <cstdlib>
 #include <mutex>
 
 #include "common.hpp"
@@ -261,6 +262,7 @@ struct NormRopeArgs {
   const float2* tab;   // rotary (cos, sin): frame [T][22], row [H][21], column [W][21]
   int S, H, W, offH, offW, heads;
   float inv_d, eps;
+  unsigned spin_limit, read_limit;  // bounds of the two waits (kSpinLimit, kReadLimit)
   unsigned* ctl;       // [0] tile counter, [1] error word (a wait hit the spin limit)
   unsigned* arrive;    // [ntm][2] published Q and K wave columns per token block
   uint64_t* partial;   // [2 heads][M] (1 << 32 | sum-of-squares bits) per wave column (Q heads, then K heads) and token
@@ -373,7 +375,7 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
           while (!late && __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                               static_cast<unsigned>(na.heads)) {
             __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) late = 1;
+            if (++spins > na.spin_limit) late = 1;
           }
         }
         late_sh = late;
@@ -398,7 +400,7 @@ qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, 
           }
           ssum = sc;
           if (__all(ready)) break;
-          if (tries > kReadLimit) bad = true;
+          if (tries > na.read_limit) bad = true;
           __builtin_amdgcn_s_sleep(2);
         }
         if (bad && lane == 0) atomicOr(na.ctl + 1, 1u);
@@ -544,6 +546,14 @@ hipError_t launch_qkv_proj_norm_rope(const void* x, const void* w, const void* b
   na.heads = heads;
   na.inv_d = 1.0f / static_cast<float>(D);
   na.eps = eps;
+  // The waits' bounds; WAN_PROJ_NORM_SPIN_LIMIT overrides both (tests force the
+  // time-out path with it; every wait still ends).
+  na.spin_limit = kSpinLimit;
+  na.read_limit = kReadLimit;
+  if (const char* env = std::getenv("WAN_PROJ_NORM_SPIN_LIMIT")) {
+    const unsigned long v = std::strtoul(env, nullptr, 10);
+    na.spin_limit = na.read_limit = static_cast<unsigned>(v < kSpinLimit ? v : kSpinLimit);
+  }
   na.ctl = reinterpret_cast<unsigned*>(ws);
   na.arrive = reinterpret_cast<unsigned*>(ws + fw.arrive_off);
   na.partial = reinterpret_cast<uint64_t*>(ws + fw.partial_off);
