@@ -97,6 +97,25 @@ def test_nan_scalars_are_rejected_by_the_built_library():
     assert lib.wan_qknorm_rope_quant_fp8(None, None, None, 0, 2, 8, 8, 2, 128, 1e-6, nan, None, None, None, None,
                                          None) == -9
     assert lib.wan_attn_fwd(None, None, None, 0, 16, 2, 128, 0.088, None) == 0
+    assert lib.wan_qkv_proj_norm_rope(None, None, None, None, None, None, None, 0, 0, 2, 8, 8, 2, 128, nan, 1e4,
+                                      None) == -9
+    assert lib.wan_qkv_proj_norm_rope(None, None, None, None, None, None, None, 0, 0, 2, 8, 8, 2, 128, 1e-6, nan,
+                                      None) == -9
+    assert lib.wan_qkv_proj_norm_rope(None, None, None, None, None, None, None, 0, 0, 2, 8, 8, 2, 128, 1e-6, 1e4,
+                                      None) == 0
+
+
+def test_fused_projection_workspace_size():
+    """wan_qkv_proj_norm_rope_workspace_bytes (pure host arithmetic): 256
+    control bytes, two arrival counts per 256-token block rounded up to 256
+    bytes, then 2*heads 8-byte words per token; -1 for invalid sizes."""
+    lib = _built_lib()
+    f = lib.wan_qkv_proj_norm_rope_workspace_bytes
+    assert f(1, 16, 2, 128) == 256 + 256 + 16 * 2 * 2 * 8
+    assert f(2, 32760, 40, 128) == 256 + ((8 * 256 + 255) // 256) * 256 + 65520 * 80 * 8
+    assert f(0, 0, 1, 128) == 256  # no token blocks: the control bytes only
+    assert f(1, 16, 2, 64) == -1 and f(-1, 16, 2, 128) == -1 and f(1, 16, 0, 128) == -1
+    assert f(1 << 40, 1 << 30, 40, 128) == -1  # overflow
 
 
 def test_fp8_binding_checks_buffer_and_output_shapes():
