@@ -63,6 +63,20 @@ def test_small_every_token(B, grid, heads):
     _check(x, w, b, gq, gk, grid, heads, f"B{B} {grid} h{heads}")
 
 
+def test_random_shapes_against_the_two_calls():
+    """24 seeded shapes (1-12 heads, odd and even; grids of 1 to ~2,500
+    tokens; with and without bias): V bit-equal to the projection's, Q and K
+    in the candidate sets of the oracle's norm + RoPE of the projection's
+    output, the error word clear."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        heads = int(rng.integers(1, 13))
+        grid = tuple(int(v) for v in rng.integers(1, [5, 24, 24]))
+        B = int(rng.integers(1, 3))
+        x, w, b, gq, gk = _inputs(B, grid, heads, seed=100 + case)
+        _check(x, w, b, gq, gk, grid, heads, f"case {case}: B{B} {grid} h{heads}", bias=bool(case % 3))
+
+
 def test_wide_model():
     """64 heads (D = 8192: a Q unit of 32 tiles, 128 K steps) on a few tokens:
     every output against the oracle."""
