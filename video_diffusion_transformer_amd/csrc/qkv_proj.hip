@@ -6,22 +6,26 @@
 //
 // Design (gfx950):
 //   * workgroup = 8 waves, output tile 256 tokens x 256 features, K in steps of
-//     64 through two LDS stages of 64 KB, filled straight from global memory
-//     by buffer_load_dwordx4 ... lds (no staging registers). The buffer form
-//     takes one descriptor per operand tile and a 32-bit offset per lane, and
-//     rows past the end of the matrix read as zeros. (The global_load_lds form
-//     of the same copy measured slower: its requests queue behind the LDS
-//     commands of the fragment reads.)
+//     64 channels; the x tiles (32 KB per step) go through three LDS stages and
+//     are copied two steps ahead, the W tiles through two, one step ahead (all
+//     160 KB of the CU's LDS). The stages are filled straight from global
+//     memory by buffer_load_dwordx4 ... lds (no staging registers), one buffer
+//     descriptor per operand tile and a 32-bit offset per lane; rows past the
+//     end of the matrix read as zeros. The copies are inline asm, waited for
+//     only by the loop's explicit vmcnt waits (the compiler's own tracking of
+//     them added waits that cancelled the deeper prefetch). (The
+//     global_load_lds form of the copy measured slower: its requests queue
+//     behind the LDS commands of the fragment reads.)
 //   * the tile is computed transposed, C^T = W X^T (A = 16 features x 32
 //     channels of W, B = 32 channels x 16 tokens of x), so each lane ends with 4
 //     consecutive features of one token;
 //   * waves are 2 (features) x 4 (tokens), each owning 128 x 64 outputs = 32
 //     MFMA tiles; per 32-channel half step a wave reads 8 W and 4 x fragments
 //     (16 B per lane) and issues 32 MFMAs;
-//   * the copies of the next step are spread over the first half's MFMAs, one
-//     per two MFMAs: issued in one burst, the copies of all waves fill the
-//     texture unit's queues and the in-order wave stalls with its MFMAs behind
-//     them (+5%);
+//   * the copies (W of the next step, x of the one after) are spread over the
+//     first half's MFMAs, one per four: issued in one burst, the copies of all
+//     waves fill the texture unit's queues and the in-order wave stalls with
+//     its MFMAs behind them;
 //   * 128-byte LDS rows (64 channels) with the 16-byte chunk XOR-swizzled by
 //     the row (p_swz): conflict-free fragment reads;
 //   * epilogue through LDS: the tile is written to LDS and stored as whole
@@ -31,11 +35,14 @@
 //     atomic counter in token-block order (token block, then feature tile):
 //     the ~4 token blocks in flight share their x tiles in L2 while W (157 MB
 //     at D = 5120) streams from the 256 MB last-level cache. Measured against
-//     one workgroup per tile in an XCD-grouped order (interleaved calls):
-//     480p (10.3 TFLOP) 7.90 against 7.80 ms, 720p (23.8 TFLOP) 18.2 against
-//     18.9 ms; the fused norm + RoPE epilogue below needs the persistent grid.
+//     one workgroup per tile in an XCD-grouped order (interleaved calls, both
+//     with two stages per operand): 480p (10.3 TFLOP) 7.90 against 7.80 ms,
+//     720p (23.8 TFLOP) 18.2 against 18.9 ms; the fused norm + RoPE epilogue
+//     below needs the persistent grid. Per-XCD queues of 4 x 8 tile blocks
+//     (fewer L2 misses) measured 1.5% slower than this order.
 #include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -50,11 +57,21 @@ static_assert(kPM == kFusedTileTokens && kPN == kFusedTileFeatures, "workspace l
 constexpr int kPWaves = 8, kPThreads = 64 * kPWaves;
 constexpr int kPRow = kPK * 2;                 // bytes per LDS row
 constexpr int kPTile = kPM * kPRow;            // 32 KB per operand tile
-constexpr int kPStage = 2 * kPTile;            // W tile + x tile
+constexpr int kXStages = 3, kWStages = 2;      // x tiles are copied two steps ahead, W tiles one
+constexpr int kWOff = kXStages * kPTile;       // the W stages follow the x stages
+constexpr int kSmem = (kXStages + kWStages) * kPTile;  // 160 KB: all of a CU's LDS
 constexpr int kPBlk = kPTile / 1024 / kPWaves;  // 1 KB blocks (8 rows) per wave per operand tile (4)
 constexpr int kPLoads = 2 * kPBlk;             // copies per wave per step (8)
+// Between two tiles the stages are free: the epilogue's LDS tile takes the
+// first 128 KB, the fused epilogue's exchange area and the tile index sit in the
+// last W stage (first written by step 0's copies, after every wave has read the
+// tile index).
+constexpr int kAuxOff = 4 * kPTile;
+constexpr int kTileShOff = kSmem - 16;
 static_assert(kPM == kPN, "one staging layout serves both operands");
-static_assert(kPWaves * 64 * 256 <= 2 * kPStage, "the epilogue needs 16 KB per wave");
+static_assert(kPWaves * 64 * 256 <= kAuxOff, "the epilogue needs 16 KB per wave below the exchange area");
+static_assert(kAuxOff + (kPWaves * 64 + 1) * 4 <= kTileShOff, "exchange area and tile index apart");
+static_assert(kWOff + (kWStages - 1) * kPTile <= kAuxOff, "exchange area and tile index in the last W stage");
 constexpr int kWaitVm0 = 0x0f70;               // s_waitcnt vmcnt(0), other counters unconstrained
 
 // XOR swizzle of the 16-byte chunk of a 128-byte row: r1 | r2 << 1 | (r0 ^ r3)
@@ -67,7 +84,33 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Buffer descriptor of `bytes` bytes from base (raw buffer, no stride): reads
+// past the end return zeros. Wave-uniform.
+__device__ __forceinline__ u32x4_t buf_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t d;
+  d[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  d[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const unsigned char*)p));
+}
+
+// One direct global -> LDS copy, 16 bytes per lane (lane l lands at lds + 16 l).
+// Written as inline asm so that the compiler does not track it: for its own
+// form of this copy the compiler cannot tell one stage from another and waits
+// for every copy in flight before the next LDS read, which undoes a prefetch
+// distance of two steps (measured: the three-stage loop 12% slower than two
+// stages with the builtin, 5% faster with this). The only waits for these
+// copies are the explicit vmcnt waits of the K loop.
+__device__ __forceinline__ void dma16(const u32x4_t& desc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(desc), "s"(soff), "{m0}"(lds));
+}
 
 // The 256 x 256 tile (m0, n0) of x W^T (no bias) into acc: each lane ends with
 // 4 consecutive features of one token per MFMA tile (i, j) -- features
@@ -85,23 +128,24 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ x, const 
   // descriptor per operand tile, sized to the rows that exist: rows past N or
   // M read as zeros (and are never stored).
   const uint32_t wbytes = (uint32_t)(min(N - n0, kPN) * K * 2), xbytes = (uint32_t)(min(M - m0, kPM) * K * 2);
-  const __amdgpu_buffer_rsrc_t wrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w + (int64_t)n0 * K), (short)0, (int)wbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (int64_t)m0 * K), (short)0, (int)xbytes, 0x00020000);
+  const u32x4_t wrs = buf_desc(w + (int64_t)n0 * K, wbytes), xrs = buf_desc(x + (int64_t)m0 * K, xbytes);
   uint32_t goff[kPBlk];
 #pragma unroll
   for (int j = 0; j < kPBlk; ++j) {
     const int r = 8 * (kPBlk * wave + j) + (lane >> 3);
     goff[j] = (uint32_t)(r * K * 2 + 16 * ((lane & 7) ^ p_swz(r)));
   }
-  auto issue = [&](int kt, int stage) {
-    unsigned char* dst = smem + stage * kPStage + kPBlk * wave * 1024;
-#pragma unroll
-    for (int j = 0; j < kPBlk; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr_t)(dst + j * 1024), 16, goff[j], kt * kPRow, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr_t)(dst + kPTile + j * 1024), 16, goff[j], kt * kPRow, 0, 0);
-    }
+  const int nk = K / kPK;
+  const uint32_t lds0 = lds_addr(smem);
+  // Block j of step kt (clamped to the last step: past it, the copies reload
+  // the last step into a stage nobody reads any more) into the x or W stage.
+  auto copy_x = [&](int j, int kt, int stage) {
+    dma16(xrs, goff[j], (uint32_t)(min(kt, nk - 1) * kPRow),
+          __builtin_amdgcn_readfirstlane(lds0 + stage * kPTile + (kPBlk * wave + j) * 1024));
+  };
+  auto copy_w = [&](int j, int kt, int stage) {
+    dma16(wrs, goff[j], (uint32_t)(min(kt, nk - 1) * kPRow),
+          __builtin_amdgcn_readfirstlane(lds0 + kWOff + stage * kPTile + (kPBlk * wave + j) * 1024));
   };
 
   // Fragment reads: lane (l16, grp) reads row 16 t + l16 at logical chunk 4 s +
@@ -116,55 +160,75 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ x, const 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{};
 
-  // Step kt lives in stage kt & 1. Iteration kt copies step kt + 1 (past the
-  // last step: the last step again, into the stage nobody reads any more), so
-  // the loop body is one basic block the schedule below can arrange.
-  const int nk = K / kPK;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Step kt reads x from stage kt % 3 and W from stage kt % 2, and copies x of
+  // step kt + 2 and W of step kt + 1 into the stages step kt - 1 read. (x two
+  // steps ahead and W one measured 3.5% faster than one step for both, W two
+  // and x one 2.8%; two steps for both would need 192 KB.) Each wave copies W
+  // first: loads complete in order, so at the top of step kt everything but its
+  // last kPBlk copies (x of step kt + 1) has landed -- x and W of step kt.
+#pragma unroll
+  for (int j = 0; j < kPBlk; ++j) copy_w(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kPBlk; ++j) copy_x(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kPBlk; ++j) copy_x(j, 1, 1);
+
+  auto step = [&](int kt, auto u_c) {
+    constexpr int u = decltype(u_c)::value;  // kt % 6: the stages are constants
+    constexpr int xc = u % kXStages, xn = (u + 2) % kXStages, wc = u % kWStages, wn1 = (u + 1) % kWStages;
     // This wave's copies of step kt have landed; past the barrier, every
-    // wave's, and every wave has finished reading step kt - 1, whose stage is
+    // wave's, and every wave has finished step kt - 1, whose stages are
     // refilled below. A bare barrier: the fence of __syncthreads() adds nothing
     // the explicit wait does not.
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0 | kPBlk);
     asm volatile("s_barrier" ::: "memory");
-    const unsigned char* st = smem + (kt & 1) * kPStage;
+    const unsigned char* stx = smem + xc * kPTile;
+    const unsigned char* stw = smem + kWOff + wc * kPTile;
     bf16x8_t a[2][8], b[2][4];
     auto read = [&](int s) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        a[s][i] = *reinterpret_cast<const bf16x8_t*>(st + (128 * wn + 16 * i) * kPRow + roff[s]);
+        a[s][i] = *reinterpret_cast<const bf16x8_t*>(stw + (128 * wn + 16 * i) * kPRow + roff[s]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[s][j] = *reinterpret_cast<const bf16x8_t*>(st + kPTile + (64 * wm + 16 * j) * kPRow + roff[s]);
+        b[s][j] = *reinterpret_cast<const bf16x8_t*>(stx + (64 * wm + 16 * j) * kPRow + roff[s]);
     };
-    auto mfmas = [&](int s) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[s][i], b[s][j], acc[i][j]);
-    };
-    // The copies follow the first half's fragment reads in program order (the
-    // compiler cannot tell the stages apart and keeps LDS reads and LDS-writing
-    // copies in order) and interleave with its MFMAs; the second half's reads
-    // follow the copies.
+    // Order, pinned by scheduling barriers: the first half's fragment reads,
+    // its 32 MFMAs with one copy after every four (W, then x: spread over the
+    // half they take 2-3% less time than one per two MFMAs or one per eight),
+    // the second half's reads after its 16th MFMA, then the second half's MFMAs.
     read(0);
-    issue(min(kt + 1, nk - 1), (kt + 1) & 1);
-    mfmas(0);
-    read(1);
-    mfmas(1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // 12 fragment reads
 #pragma unroll
-    for (int q = 0; q < kPLoads; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // 1 copy
+    for (int m = 0; m < 64; ++m) {
+      const int sh = m >> 5, i = (m & 31) >> 2, j = m & 3;
+      acc[i][j] = mfma16(a[sh][i], b[sh][j], acc[i][j]);
+      if (m == 15) {
+        __builtin_amdgcn_sched_barrier(0);
+        read(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (m % 4 == 3 && m < 4 * kPLoads) {
+        const int q = m / 4;
+        __builtin_amdgcn_sched_barrier(0);
+        if (q < kPBlk)
+          copy_w(q, kt + 1, wn1);
+        else
+          copy_x(q - kPBlk, kt + 2, xn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 64 - 2 * kPLoads, 0);
-    __builtin_amdgcn_sched_barrier(0);  // nothing moves past the next iteration's wait
+    __builtin_amdgcn_sched_barrier(0);  // nothing moves past the next step's wait
+  };
+  for (int kt = 0; kt < nk; kt += 6) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
+    if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3>{});
+    if (kt + 4 < nk) step(kt + 4, std::integral_constant<int, 4>{});
+    if (kt + 5 < nk) step(kt + 5, std::integral_constant<int, 5>{});
   }
-  // The last copies (a reload) land, and every wave leaves the stages, before
-  // the epilogue reuses the LDS.
+  // Every copy (the last ones reload the last step) lands, and every wave
+  // leaves the stages, before the epilogue reuses the LDS.
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 }
@@ -280,9 +344,12 @@ template <bool Norm>
 __global__ void __launch_bounds__(kPThreads, 1)
 qkv_proj_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
                 uint16_t* __restrict__ out, int M, int N, int K, int ntm, int ntn, NormRopeArgs na) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kPStage];
-  __shared__ int tile_sh, late_sh;  // the tile taken; its arrival wait timed out
-  __shared__ float xsum[kPWaves][64];  // sums of squares passed between the two waves of a row
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  int& tile_sh = *reinterpret_cast<int*>(smem + kTileShOff);  // the tile taken
+  // Fused epilogue only: sums of squares passed between the two waves of a
+  // row, and whether the arrival wait timed out.
+  float(&xsum)[kPWaves][64] = *reinterpret_cast<float(*)[kPWaves][64]>(smem + kAuxOff);
+  int& late_sh = *reinterpret_cast<int*>(smem + kAuxOff + sizeof(xsum));
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
