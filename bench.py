@@ -359,6 +359,21 @@ def run_steps(w, dev, steps, warmup, fp8_unfused=False):
          "norm": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
          "quant": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
          "attn": sum(e[2].elapsed_time(e[3]) for e in evs) / steps}
+    if not fp8:
+        # a plain device copy of the norm's bytes (Q and K read, then written):
+        # the bandwidth the chip reaches on a read + write stream of this size
+        dst = torch.empty_like(pristine_qk)
+        dst.copy_(pristine_qk)
+        torch.cuda.synchronize()
+        e0, e1 = E(), E()
+        reps = max(3, steps)
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(pristine_qk)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t["copy"] = e0.elapsed_time(e1) / reps
+        del dst
     if fp8:
         # the single-pass producer with delayed scales, on the same raw input:
         # amax_prev from the last step (what the previous DiT step would report)
@@ -415,6 +430,11 @@ def kernel_objects(w, t, fp8_unfused=False):
                                "frac": round(gbs / PEAK_HBM_GBS, 4), "ms_per_launch": round(t["norm"], 4),
                                "bytes_per_launch": w.norm_bytes(),
                                "traffic": committed_traffic("qknorm_rope", w.name)}
+        if "copy" in t:
+            cbs = w.norm_bytes() / (t["copy"] * 1e-3) / 1e9
+            objs["qknorm_rope"].update({"copy_GBps": round(cbs, 1), "frac_of_copy": round(gbs / cbs, 4),
+                                        "copy_note": "device copy (torch copy_) of the same bytes: Q and K "
+                                                     "of every token read once and written once"})
         if fp8:
             objs["quant_ms_per_launch"] = round(t["quant"], 4)
     return objs
@@ -488,6 +508,10 @@ def main():
         "roofline": objs.pop("attention"),
     }
     rec.update(objs)
+    props = torch.cuda.get_device_properties(dev)
+    rec["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "compute_units": props.multi_processor_count,
+                     "hbm_GiB": round(props.total_memory / 2**30, 1)}
     if args.ring_cp:
         ring = ring_share(w, qkv, args.ring_cp)
         if ring:
