@@ -105,9 +105,10 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 // Written as inline asm so that the compiler does not track it: for its own
 // form of this copy the compiler cannot tell one stage from another and waits
 // for every copy in flight before the next LDS read, which undoes a prefetch
-// distance of two steps (measured: the three-stage loop 12% slower than two
-// stages with the builtin, 5% faster with this). The only waits for these
-// copies are the explicit vmcnt waits of the K loop.
+// distance of two steps (measured at 480p: the three-stage loop 12% slower
+// than two stages with the builtin, 3.5% faster with this, 5% with the copies
+// spread as below). The only waits for these copies are the explicit vmcnt
+// waits of the K loop.
 __device__ __forceinline__ void dma16(const u32x4_t& desc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(desc), "s"(soff), "{m0}"(lds));
 }
@@ -194,9 +195,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ x, const 
         b[s][j] = *reinterpret_cast<const bf16x8_t*>(stx + (64 * wm + 16 * j) * kPRow + roff[s]);
     };
     // Order, pinned by scheduling barriers: the first half's fragment reads,
-    // its 32 MFMAs with one copy after every four (W, then x: spread over the
-    // half they take 2-3% less time than one per two MFMAs or one per eight),
-    // the second half's reads after its 16th MFMA, then the second half's MFMAs.
+    // its 32 MFMAs with one copy after every four (W, then x; measured 2-4%
+    // faster than one copy per two, three, five or eight MFMAs), the second
+    // half's reads after the first half's 16th MFMA, then the second half's
+    // 32 MFMAs.
     read(0);
 #pragma unroll
     for (int m = 0; m < 64; ++m) {
