@@ -123,9 +123,11 @@ int wan_token_grid(int64_t width, int64_t height, int64_t num_frames, int64_t *T
  *          input.
  * Arithmetic: bf16 products accumulated in fp32 (gfx950 MFMA), bias added in
  * fp32, one round-to-nearest-even to bf16.
- * Launch: a persistent grid taking output tiles from a 16-byte device counter,
- * one per call from a ring of 65,536 per device that the library allocates
- * (1 MB) on the first call on the device and keeps until the process ends.
+ * Launch: a persistent grid taking output tiles from a 32-byte block of
+ * device counters (per-XCD tile queues when the 3*D output features form 57
+ * to 64 tiles of 256, as at D = 5120; else one counter), one block per call
+ * from a ring of 65,536 per device that the library allocates (2 MB) on the
+ * first call on the device and keeps until the process ends.
  * Errors: WAN_E_NULL, WAN_E_SHAPE, WAN_E_UNSUPPORTED, WAN_E_ALIGN (16-byte),
  * WAN_E_ALIAS, WAN_E_OVERFLOW (also B*S above 2^31 - 257 token rows),
  * WAN_E_NOMEM (the counter), WAN_E_HIP.

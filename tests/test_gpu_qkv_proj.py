@@ -42,8 +42,12 @@ def _check(gpu, x, w, b, what):
 
 
 @pytest.mark.parametrize("B,S,heads,with_bias", [(1, 1, 1, True), (1, 77, 2, False), (2, 300, 2, True),
-                                                 (1, 513, 3, True), (1, 256, 1, False)])
+                                                 (1, 513, 3, True), (1, 256, 1, False),
+                                                 (1, 700, 40, True), (2, 1100, 40, False)])
 def test_small_full(B, S, heads, with_bias):
+    """Every output. With 40 heads (60 feature tiles in 8 bands) the tiles come
+    from the per-XCD queues, here with block rows of 3 and of 9 token tiles
+    (ragged: a block row holds 4)."""
     D = heads * 128
     x = synth.make_tokens(B, S, D, seed=S + heads)
     w, b = synth.make_qkv_weights(D, seed=S + heads)

@@ -52,9 +52,10 @@ int rope_table(int64_t T, int64_t H, int64_t W, float theta, hipStream_t stream,
 }
 
 // --------------------------------------------------- projection tile counters
-// The persistent projection takes its tiles from a 16-byte device counter that
-// the launch clears first. Each call takes the next slot of a ring of 65,536
-// counters per device (1 MB, allocated on the first call on the device and
+// The persistent projection takes its tiles from a 32-byte block of device
+// counters (one per XCD queue) that the launch clears first. Each call takes
+// the next slot of a ring of 65,536 per device (2 MB, allocated on the first
+// call on the device and
 // kept until the process ends), so calls on different streams, or on a stream
 // handle reused after a destroy, never share a counter unless 65,536 calls
 // are in flight at once.
@@ -70,11 +71,11 @@ int proj_counter(unsigned** out) {
   std::lock_guard<std::mutex> lock(g_cnt_mu);
   if (!g_counter_ring[dev]) {
     void* p = nullptr;
-    if (hipMalloc(&p, static_cast<size_t>(kCounterSlots) * 16) != hipSuccess) return WAN_E_NOMEM;
+    if (hipMalloc(&p, static_cast<size_t>(kCounterSlots) * 32) != hipSuccess) return WAN_E_NOMEM;
     g_counter_ring[dev] = static_cast<unsigned char*>(p);
   }
   const uint32_t slot = g_counter_next[dev]++ % kCounterSlots;
-  *out = reinterpret_cast<unsigned*>(g_counter_ring[dev] + static_cast<size_t>(slot) * 16);
+  *out = reinterpret_cast<unsigned*>(g_counter_ring[dev] + static_cast<size_t>(slot) * 32);
   return WAN_OK;
 }
 
