@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libwan_attn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "noalloc.hip", "qkv_proj.hip", "qknorm_rope.hip", "attn_fwd.hip", "attn_fwd_exact.hip",
-           "attn_merge.hip", "quant_fp8.hip", "attn_fwd_fp8.hip"]
+           "attn_fwd_ring_small.hip", "attn_merge.hip", "quant_fp8.hip", "attn_fwd_fp8.hip"]
 
 
 def hipcc():
@@ -52,12 +52,21 @@ SCHED_FLAGS = {
 }
 
 
+# Per-source definitions: the ring-attention instances with two 16-query tiles
+# per wave (256 queries per workgroup) for grids that fill the CUs badly with
+# 384 (attn_fwd_exact.hip chooses per launch).
+DEFINES = {
+    "attn_fwd_ring_small.hip": ["-DWAN_ATTN_QT=2"],
+}
+
+
 def kernel_flags(src):
     """Kernel sources may assume no NaN arithmetic (max/min then need no NaN
     canonicalisation; NaN inputs give unspecified results). The host-side
     entry points (api.cpp) are built without that assumption, so their checks
-    of scalar arguments still see a NaN. Plus the source's scheduler flags."""
-    return [] if src.endswith(".cpp") else ["-fno-honor-nans", *SCHED_FLAGS.get(src, [])]
+    of scalar arguments still see a NaN. Plus the source's scheduler flags and
+    definitions."""
+    return [] if src.endswith(".cpp") else ["-fno-honor-nans", *SCHED_FLAGS.get(src, []), *DEFINES.get(src, [])]
 
 
 def _compile(src):

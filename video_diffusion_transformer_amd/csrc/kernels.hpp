@@ -50,6 +50,13 @@ hipError_t launch_attn_fwd_chunk(const void* q_src, int Sq, const void* kv_src, 
 hipError_t launch_attn_fwd_chunk_fold(const void* q_src, int Sq, const void* kv_src, int Skv, float* acc,
                                       float* acc_lse, void* out16, int B, int heads, float softmax_scale,
                                       hipStream_t stream);
+
+// The same two launches with 256 queries per workgroup (attn_fwd_ring_small.hip).
+hipError_t launch_attn_fwd_chunk_q256(const void* q_src, int Sq, const void* kv_src, int Skv, float* out, float* lse,
+                                      int B, int heads, float softmax_scale, hipStream_t stream);
+hipError_t launch_attn_fwd_chunk_fold_q256(const void* q_src, int Sq, const void* kv_src, int Skv, float* acc,
+                                           float* acc_lse, void* out16, int B, int heads, float softmax_scale,
+                                           hipStream_t stream);
 hipError_t launch_attn_merge(float* acc, float* acc_lse, const float* chunk, const float* chunk_lse, void* out16,
                              int B, int Sq, int heads, hipStream_t stream);
 
