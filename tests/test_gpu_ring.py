@@ -10,8 +10,9 @@ import pytest
 import torch
 
 from oracle import wan_ref
-from tests.parity import BF16_GATES, LSE_ABS, assert_gates, attn_error_stats
+from tests.parity import BF16_GATES, LSE_ABS, assert_gates, attn_error_stats, sample_rows
 from video_diffusion_transformer_amd import synth, wan_attn
+from video_diffusion_transformer_amd.configs import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +184,46 @@ def test_chunk_errors():
     with pytest.raises(wan_attn.WanError) as e:  # merging a buffer into itself
         wan_attn.attn_merge(o, l, o, l, 2)
     assert e.value.status == -5
+
+
+def test_full_480p_share_cp8_sampled_rows():
+    """One rank's share of ring attention at the 480p shape with CP = 8, as the
+    benchmark runs it: the first 4,095 queries of each (b, h) attend the 8 K/V
+    chunks of 4,095 keys, each folded into the accumulator in the attention
+    epilogue (wan_attn_fwd_chunk_merge; at this size with 256 queries per
+    workgroup). For every (b, h), seeded rows plus the edges of both workgroup
+    sizes, against the oracle's attention over all 32,760 keys."""
+    w = WORKLOADS["480p"]
+    cp = 8
+    sq = w.S // cp
+    assert sq * cp == w.S
+    qkv = synth.make_qkv(w.B, w.S, w.heads, seed=w.seed, device=DEV)
+    shard = qkv[:, :sq].contiguous()
+    acc = torch.empty((w.B, sq, w.D), dtype=torch.float32, device=DEV)
+    acc_lse = torch.full((w.B, w.heads, sq), -math.inf, dtype=torch.float32, device=DEV)
+    out16 = torch.empty((w.B, sq, w.D), dtype=torch.bfloat16, device=DEV)
+    for c in range(cp):
+        chunk = qkv[:, c * sq:(c + 1) * sq].contiguous()
+        wan_attn.attn_fwd_chunk_merge(shard, chunk, acc, acc_lse, w.heads, out_bf16=out16 if c == cp - 1 else None)
+        del chunk
+    torch.cuda.synchronize()
+    rows = sample_rows(sq, 48, seed=11, bms=(256, 384))
+    assert rows.min() >= 0 and rows.max() < sq  # host-side bounds check before the GPU gather
+    rows_t = torch.from_numpy(rows).to(DEV)
+    got = _np(out16.index_select(1, rows_t))
+    got_lse = _np(acc_lse.index_select(2, rows_t))
+    host = qkv.cpu()
+    del qkv, shard, acc, acc_lse, out16
+    worst = {"max": 0.0, "lse": 0.0}
+    for b in range(w.B):
+        for h in range(w.heads):
+            q = host[b, rows, h * 128:(h + 1) * 128].double().numpy()
+            k = host[b, :, w.D + h * 128:w.D + (h + 1) * 128].double().numpy()
+            v = host[b, :, 2 * w.D + h * 128:2 * w.D + (h + 1) * 128].double().numpy()
+            o_ref, l_ref = wan_ref.attention_ref(q, k, v, SCALE)
+            st = attn_error_stats(got[b, :, h * 128:(h + 1) * 128], o_ref)
+            assert_gates(st, BF16_GATES, f"ring share b{b} h{h}")
+            le = float(np.abs(got_lse[b, h] - l_ref).max())
+            assert le <= LSE_ABS, (b, h, le)
+            worst = {"max": max(worst["max"], st["max"]), "lse": max(worst["lse"], le)}
+    print(f"480p ring share, cp = {cp}: {len(rows)} rows x {w.B * w.heads} (b, h): worst {worst}")
